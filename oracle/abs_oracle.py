@@ -1,0 +1,382 @@
+"""Float64 CPU oracle: 3D video blocking, pooled Top-p routing with a Top-k
+floor and own-block repair, slack fill, and block-sparse softmax attention.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Product code must not
+import this module.
+
+Sources.  "FVAttn explainer" is the web page titled (in Chinese) "FVAttn:
+adaptive sparse attention with runtime load balancing, for video generation",
+an explainer of arXiv 2607.16190 "Adaptive Sparse Attention with Runtime Load
+Balancing for Video Generation".  Its sections cited here: "The real problem",
+"Core method" parts 1 (sparse-routing frontend), 2 (runtime load balancing) and
+3 (slack-aware sparse augmentation), "Highlights and limitations", and "Lessons
+for engineering".  The pages leave several steps open; each place where this
+module picks a reading says so in its docstring ("Reading:").
+
+Conventions.
+* Inputs Q, K, V are [B, N, H, d] with tokens in row-major (t, h, w) order over
+  the real latent grid (T, H, W).  Values are upcast to float64 on entry.
+* Rows of the block mask are indexed r = (b * H + h) * nb + i (query block i).
+"""
+from __future__ import annotations
+
+import dataclasses
+import functools
+import math
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# 3D video blocks
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class Geometry:
+    grid: tuple        # (T, H, W) real latent grid
+    block: tuple       # (bt, bh, bw)
+    nblk: tuple        # blocks along each axis
+    padded: tuple      # grid rounded up to whole blocks
+    nb: int            # blocks per head
+    bt_tokens: int     # tokens per block, bt * bh * bw
+
+    @property
+    def tokens(self) -> int:
+        return self.grid[0] * self.grid[1] * self.grid[2]
+
+
+def geometry(grid: Sequence[int], block: Sequence[int]) -> Geometry:
+    """Block grid of a (T, H, W) latent video cut into (bt, bh, bw) blocks.
+
+    Source: FVAttn explainer, "Core method" part 1, bullet on video-aware block
+    organisation (tokens regrouped into 3D blocks that follow spatio-temporal
+    locality) and "Lessons for engineering" item 4 (3D blocks rather than 1D
+    chunks).  Reading: each axis is padded up to a whole number of blocks; the
+    padding tokens do not exist in the input and never take part in pooling or
+    attention.
+    """
+    grid = tuple(int(x) for x in grid)
+    block = tuple(int(x) for x in block)
+    nblk = tuple(-(-g // b) for g, b in zip(grid, block))
+    padded = tuple(n * b for n, b in zip(nblk, block))
+    return Geometry(grid, block, nblk, padded, nblk[0] * nblk[1] * nblk[2],
+                    block[0] * block[1] * block[2])
+
+
+def token_block_slot(t: int, h: int, w: int, geo: Geometry):
+    """(block, slot) of latent token (t, h, w).
+
+    Reading: blocks are numbered row-major over the block grid and slots
+    row-major inside a block; query and key blocks share this one blocking, so
+    "own block" of query block i is key block i.
+    """
+    bt, bh, bw = geo.block
+    _, nbh, nbw = geo.nblk
+    blk = ((t // bt) * nbh + h // bh) * nbw + w // bw
+    slot = ((t % bt) * bh + h % bh) * bw + w % bw
+    return blk, slot
+
+
+@functools.lru_cache(maxsize=16)
+def _members_cached(grid: tuple, block: tuple) -> np.ndarray:
+    geo = geometry(grid, block)
+    T, H, W = geo.grid
+    table = np.full((geo.nb, geo.bt_tokens), -1, dtype=np.int64)
+    for t in range(geo.padded[0]):
+        for h in range(geo.padded[1]):
+            for w in range(geo.padded[2]):
+                blk, slot = token_block_slot(t, h, w, geo)
+                if t < T and h < H and w < W:
+                    table[blk, slot] = (t * H + h) * W + w
+    table.setflags(write=False)
+    return table
+
+
+def block_members(geo: Geometry) -> np.ndarray:
+    """[nb, bt_tokens] token index n = (t*H + h)*W + w of each block slot, -1 for
+    a padding slot.  Built by visiting every padded coordinate once."""
+    return _members_cached(geo.grid, geo.block)
+
+
+# --------------------------------------------------------------------------
+# Routing: pooled similarity, Top-p, floor, repair
+# --------------------------------------------------------------------------
+def pool(X, geo: Geometry) -> np.ndarray:
+    """Mean of X over the valid tokens of each block: [B, H, nb, d] float64.
+
+    Source: FVAttn explainer, "Highlights and limitations" (routing scores are
+    an approximate similarity computed on a cheap draft) and part 1 (decisions
+    are made per 3D block).  Reading: the draft is the block mean of Q and of K
+    over the block's real tokens.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    B, N, H, d = X.shape
+    members = block_members(geo)
+    out = np.empty((B, H, geo.nb, d))
+    for blk in range(geo.nb):
+        idx = members[blk][members[blk] >= 0]
+        out[:, :, blk, :] = X[:, idx, :, :].mean(axis=1)
+    return out
+
+
+def block_probabilities(Qp: np.ndarray, Kp: np.ndarray) -> np.ndarray:
+    """P[b, h, i, :] = softmax_j(Qp_i . Kp_j / sqrt(d)) over all key blocks j.
+
+    Source: FVAttn explainer, part 1, Top-p bullet (the kept set is measured by
+    cumulative similarity mass).  Reading: the mass is the row softmax of the
+    pooled scores, over every key block, with the usual 1/sqrt(d) scale and no
+    correction for how many real tokens a block holds.
+    """
+    d = Qp.shape[-1]
+    S = np.einsum("bhid,bhjd->bhij", Qp, Kp) / math.sqrt(d)
+    S = S - S.max(axis=-1, keepdims=True)
+    E = np.exp(S)
+    return E / E.sum(axis=-1, keepdims=True)
+
+
+def select_row(prow: np.ndarray, i: int, p: float, k_floor: int):
+    """Kept key blocks of one query-block row (ascending), plus diagnostics.
+
+    Steps (FVAttn explainer, part 1):
+      1. order the key blocks by probability, largest first; equal values keep
+         the lower block index first (reading: ties go to the lowest index);
+      2. Top-p: m = the smallest count whose cumulative mass reaches p
+         (reading: "reaches" means >= p; with p >= 1 every block is kept; if
+         rounding keeps every partial sum below p, all nb blocks are kept);
+      3. Top-k floor: never fewer than k_floor blocks (reading: the floor counts
+         key blocks of each (head, query-block) row; k_floor > nb keeps all);
+      4. repair: the query's own block is added if it is not already there
+         (reading: the repair works on the materialised set without rescoring,
+         and the own block is the hole it fills, so no row or key-block column
+         is ever empty).
+    """
+    prow = np.asarray(prow, dtype=np.float64)
+    nb = prow.shape[0]
+    order = np.argsort(-prow, kind="stable")
+    masses = prow[order]
+    if p >= 1.0:
+        m = nb
+    else:
+        csum = np.cumsum(masses)          # sequential running sum in sorted order
+        hit = np.nonzero(csum >= p)[0]
+        m = int(hit[0]) + 1 if hit.size else nb
+    m2 = min(nb, max(m, int(k_floor)))
+    kept = set(int(j) for j in order[:m2])
+    kept.add(int(i))
+    csum = np.concatenate([[0.0], np.cumsum(masses)])
+    diag = dict(m=m, m2=m2, c_prev=float(csum[m - 1]), c_at=float(csum[m]),
+                p_cut=float(masses[m2 - 1]),
+                p_next=float(masses[m2]) if m2 < nb else float("nan"))
+    return sorted(kept), diag
+
+
+def _select_head(P: np.ndarray, p: float, k_floor: int):
+    """select_row applied to every row of one head's [nb, nb] matrix at once
+    (the same steps, vectorised over rows)."""
+    nb = P.shape[0]
+    order = np.argsort(-P, axis=1, kind="stable")
+    masses = np.take_along_axis(P, order, axis=1)
+    csum = np.cumsum(masses, axis=1)
+    if p >= 1.0:
+        m = np.full(nb, nb, dtype=np.int64)
+    else:
+        hit = csum >= p
+        m = np.where(hit.any(axis=1), hit.argmax(axis=1) + 1, nb).astype(np.int64)
+    m2 = np.minimum(nb, np.maximum(m, int(k_floor)))
+    keep = np.zeros((nb, nb), dtype=bool)
+    rank = np.arange(nb)[None, :]
+    np.put_along_axis(keep, order, rank < m2[:, None], axis=1)
+    keep[np.arange(nb), np.arange(nb)] = True
+    cz = np.concatenate([np.zeros((nb, 1)), csum], axis=1)
+    rows = np.arange(nb)
+    diag = dict(m=m, m2=m2, c_prev=cz[rows, m - 1], c_at=cz[rows, m],
+                p_cut=masses[rows, m2 - 1],
+                p_next=np.where(m2 < nb, masses[rows, np.minimum(m2, nb - 1)], np.nan))
+    return keep, diag
+
+
+def row_exemptions(diag: Dict[str, np.ndarray], p: float, k_floor: int,
+                   gap: float = 1e-4, tie_rel: float = 1e-5) -> np.ndarray:
+    """True for rows whose kept set is not decided robustly in float32.
+
+    A row is exact-checked when its cumulative mass is further than ``gap`` from
+    p on both sides of the cut (or the floor decides the count), and the two
+    probabilities straddling the final cut are not a near tie
+    (0 < |P_cut - P_next| <= tie_rel * P_cut).  Exact ties are not exempt: the
+    lowest-index rule decides them on both sides.
+    """
+    m = np.asarray(diag["m"])
+    if p >= 1.0:
+        return np.zeros(m.shape, dtype=bool)
+    close = np.minimum(np.abs(diag["c_prev"] - p), np.abs(diag["c_at"] - p)) <= gap
+    close &= ~(m < k_floor)
+    dp = np.abs(diag["p_cut"] - diag["p_next"])
+    near_tie = (dp > 0) & (dp <= tie_rel * diag["p_cut"])
+    near_tie &= ~np.isnan(diag["p_next"])
+    return close | near_tie
+
+
+def slack_fill(P: np.ndarray, keep: np.ndarray, slack: float):
+    """Top up every head to a fixed budget of ceil(slack * nb^2) block pairs.
+
+    Source: FVAttn explainer, part 3 (spare capacity is filled with high-value
+    blocks) and "Lessons for engineering" item 5 (filter by score before
+    filling).  Reading: the budget is per head over all nb x nb block pairs;
+    the unkept pairs with the largest P are added, ties by lowest linear index
+    i * nb + j, until the head holds exactly the budget (a head already at or
+    above it is unchanged).
+    Returns (new_keep, info) where info[(b, h)] gives the budget, the number
+    added and the P values of the last added and first skipped candidates.
+    """
+    B, H, nb, _ = P.shape
+    out = keep.copy()
+    budget = int(math.ceil(float(slack) * nb * nb))
+    info = {}
+    for b in range(B):
+        for h in range(H):
+            flat_keep = out[b, h].reshape(-1)
+            nnz = int(flat_keep.sum())
+            need = budget - nnz
+            rec = dict(budget=budget, nnz=nnz, added=0, last=np.nan, next=np.nan)
+            if need > 0:
+                cand = np.nonzero(~flat_keep)[0]            # ascending linear index
+                vals = P[b, h].reshape(-1)[cand]
+                order = np.argsort(-vals, kind="stable")
+                take = cand[order[:need]]
+                flat_keep[take] = True
+                rec.update(added=int(need), last=float(vals[order[need - 1]]),
+                           next=float(vals[order[need]]) if need < cand.size else np.nan)
+            out[b, h] = flat_keep.reshape(nb, nb)
+            info[(b, h)] = rec
+    return out, info
+
+
+def keep_to_csr(keep: np.ndarray):
+    """CSR of a [B, H, nb, nb] boolean mask: rows (b, h, i) in order, columns
+    ascending.  Returns (row_ptr int64 [rows+1], col_idx int64, head_nnz)."""
+    B, H, nb, _ = keep.shape
+    flat = keep.reshape(B * H * nb, nb)
+    counts = flat.sum(axis=1)
+    row_ptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    col_idx = np.nonzero(flat)[1].astype(np.int64)      # row-major: ascending per row
+    head_nnz = keep.reshape(B * H, -1).sum(axis=1).astype(np.int64)
+    return row_ptr, col_idx, head_nnz
+
+
+def csr_to_keep(row_ptr, col_idx, B: int, H: int, nb: int) -> np.ndarray:
+    keep = np.zeros((B * H * nb, nb), dtype=bool)
+    row_ptr = np.asarray(row_ptr)
+    col_idx = np.asarray(col_idx)
+    for r in range(B * H * nb):
+        keep[r, col_idx[row_ptr[r]:row_ptr[r + 1]]] = True
+    return keep.reshape(B, H, nb, nb)
+
+
+def route(Q, K, geo: Geometry, p: float, k_floor: int, slack: float = 0.0):
+    """Pooled Top-p routing of every (batch, head, query-block) row.
+
+    Returns a dict with the CSR arrays, the boolean mask before and after slack
+    fill, the block probabilities and the per-row diagnostics used by the
+    float32 exemption rule.
+    """
+    Qp, Kp = pool(Q, geo), pool(K, geo)
+    P = block_probabilities(Qp, Kp)
+    B, H, nb, _ = P.shape
+    keep = np.zeros((B, H, nb, nb), dtype=bool)
+    diag = {k: np.empty((B, H, nb)) for k in ("m", "m2", "c_prev", "c_at", "p_cut", "p_next")}
+    for b in range(B):
+        for h in range(H):
+            keep[b, h], dg = _select_head(P[b, h], p, k_floor)
+            for key, val in dg.items():
+                diag[key][b, h] = val
+    base = keep
+    info = None
+    if slack > 0.0:
+        keep, info = slack_fill(P, base, slack)
+    row_ptr, col_idx, head_nnz = keep_to_csr(keep)
+    return dict(row_ptr=row_ptr, col_idx=col_idx, head_nnz=head_nnz, keep=keep,
+                base_keep=base, P=P, Qp=Qp, Kp=Kp, diag=diag, slack_info=info)
+
+
+# --------------------------------------------------------------------------
+# Attention
+# --------------------------------------------------------------------------
+def sparse_attention(Q, K, V, geo: Geometry, row_ptr, col_idx,
+                     rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Softmax attention of each query block over the union of its kept key
+    blocks: O[b, n, h, :] for the real query tokens of the given rows.
+
+    Source: FVAttn explainer, part 1 (the routed mask decides which KV blocks
+    each head keeps; attention runs over those) and "The real problem" (the
+    quadratic attention is what the sparsity removes).  Reading: one softmax
+    over all real keys of all kept blocks, scale 1/sqrt(d), padding keys and
+    padding queries absent.  Outputs of rows not computed are NaN.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, N, H, d = Q.shape
+    nb = geo.nb
+    members = block_members(geo)
+    O = np.full((B, N, H, d), np.nan)
+    row_ptr = np.asarray(row_ptr)
+    col_idx = np.asarray(col_idx)
+    todo = range(B * H * nb) if rows is None else rows
+    for r in todo:
+        b, rem = divmod(int(r), H * nb)
+        h, i = divmod(rem, nb)
+        qtok = members[i][members[i] >= 0]
+        cols = col_idx[row_ptr[r]:row_ptr[r + 1]]
+        ktok = np.concatenate([members[j][members[j] >= 0] for j in cols])
+        logits = Q[b, qtok, h, :] @ K[b, ktok, h, :].T / math.sqrt(d)
+        logits -= logits.max(axis=1, keepdims=True)
+        w = np.exp(logits)
+        w /= w.sum(axis=1, keepdims=True)
+        O[b, qtok, h, :] = w @ V[b, ktok, h, :]
+    return O
+
+
+def dense_attention(Q, K, V) -> np.ndarray:
+    """Textbook softmax(Q K^T / sqrt(d)) V per (batch, head), [B, N, H, d]."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, N, H, d = Q.shape
+    O = np.empty((B, N, H, d))
+    for b in range(B):
+        for h in range(H):
+            s = Q[b, :, h, :] @ K[b, :, h, :].T / math.sqrt(d)
+            s -= s.max(axis=1, keepdims=True)
+            w = np.exp(s)
+            w /= w.sum(axis=1, keepdims=True)
+            O[b, :, h, :] = w @ V[b, :, h, :]
+    return O
+
+
+# --------------------------------------------------------------------------
+# Work schedule
+# --------------------------------------------------------------------------
+def schedule(row_ptr, mode: str, rows_per_head: Optional[int] = None,
+             heads_per_phase: int = 1) -> np.ndarray:
+    """Order in which the (batch, head, query-block) items are processed.
+
+    Source: FVAttn explainer, part 2 (runtime load balancing: measure each
+    head's mask size before the kernel runs and hand the heaviest work out
+    first).  Reading on one GPU: items are rows of the block mask, their cost is
+    the row's kept-block count, and the compute units pull items from one queue.
+      "head_major": rows in their natural (b, h, i) order;
+      "nnz_sorted": kept-block count descending, ties by row index;
+      "head_phased": heads grouped into consecutive phases of heads_per_phase
+         heads; phases in order, inside a phase count descending, ties by row.
+    """
+    counts = np.diff(np.asarray(row_ptr, dtype=np.int64))
+    rows = counts.shape[0]
+    if mode == "head_major":
+        return np.arange(rows, dtype=np.int64)
+    if mode == "nnz_sorted":
+        return np.argsort(-counts, kind="stable").astype(np.int64)
+    if mode == "head_phased":
+        phase = (np.arange(rows) // rows_per_head) // heads_per_phase
+        return np.array(sorted(range(rows), key=lambda r: (phase[r], -counts[r], r)),
+                        dtype=np.int64)
+    raise ValueError(mode)
