@@ -1,0 +1,692 @@
+// Attention kernels: V re-layout, work schedule, and block-sparse flash-style
+// attention over the kept key blocks.  Source: FVAttn explainer ("FVAttn:
+// adaptive sparse attention with runtime load balancing, for video
+// generation"), "Core method" part 1 (attention restricted to the routed KV
+// blocks) and part 2 (runtime load balancing: per-head mask sizes measured
+// before the kernel, heaviest work first), recast from ranks to the compute
+// units of one GPU.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+// the LDS copies set M0 inside inline asm (declared as clobbered)
+#pragma clang diagnostic ignored "-Winline-asm"
+
+namespace abs_impl {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier that does not drain outstanding global loads (the HIP
+// __syncthreads() also waits for every in-flight vector memory operation,
+// which would serialise the K/V prefetch with the math).
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Key order inside each 16-key group of the re-laid V: positions 0-7 hold keys
+// {0-3, 8-11} and positions 8-15 hold keys {4-7, 12-15}, which is the order in
+// which a 32x32 MFMA accumulator hands the softmax probabilities to the next
+// MFMA as its B operand.  Swapping bits 2 and 3 maps a key to its position and
+// back.
+__host__ __device__ __forceinline__ int vt_perm(int k) {
+  return (k & ~12) | ((k >> 1) & 4) | ((k << 1) & 8);
+}
+
+// ---------------------------------------------------------------------------
+// K/V re-layout into the attention kernel's chunk-major block tiles (bf16):
+//   Kc[b, h, blk, c, key, 8]: 16-byte chunk c (d = 8c .. 8c+7) of every key;
+//   Vc[b, h, blk, c, d, 8]  : for every d, the 8 keys of key chunk c, in
+//                             vt_perm order;
+// zeros in padding slots.  A tile is then one contiguous BT*D*2-byte copy into
+// LDS, and every MFMA operand read is (lane base + compile-time offset).  One
+// workgroup per (block, b*h, K|V).
+// ---------------------------------------------------------------------------
+template <int D, int BT>
+__global__ __launch_bounds__(256) void kv_relayout_kernel(Geo g, const bf16_t* __restrict__ k,
+                                                          const bf16_t* __restrict__ v,
+                                                          bf16_t* __restrict__ kc,
+                                                          bf16_t* __restrict__ vc) {
+  constexpr int RW = D / 2 + 4;  // row stride in 32-bit words (16-byte aligned, padded)
+  __shared__ __attribute__((aligned(16))) uint32_t tile[BT * RW];
+  const int blk = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
+  const int b = bh / g.H, h = bh % g.H;
+  const int tb = blk / (g.nbh * g.nbw), hb = (blk / g.nbw) % g.nbh, wb = blk % g.nbw;
+  const int Tl = min(g.bt, g.T - tb * g.bt), Hl = min(g.bh, g.Hg - hb * g.bh),
+            Wl = min(g.bw, g.W - wb * g.bw);
+  const int plane = g.bh * g.bw;
+  const bf16_t* src = which == 0 ? k : v;
+  for (int e = threadIdx.x; e < BT * (D / 8); e += 256) {
+    const int s = e / (D / 8), c = e % (D / 8);
+    const int st = s / plane, sh = (s / g.bw) % g.bh, sw = s % g.bw;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (st < Tl && sh < Hl && sw < Wl) {
+      const long n = ((long)(tb * g.bt + st) * g.Hg + hb * g.bh + sh) * g.W + wb * g.bw + sw;
+      val = *reinterpret_cast<const uint4*>(src + (((long)b * g.N + n) * g.H + h) * D + c * 8);
+    }
+    *reinterpret_cast<uint4*>(&tile[s * RW + c * 4]) = val;
+  }
+  __syncthreads();
+  const long tile_off = ((long)bh * g.nb + blk) * (long)(D * BT);
+  if (which == 0) {
+    uint4* out = reinterpret_cast<uint4*>(kc + tile_off);
+    for (int e = threadIdx.x; e < BT * (D / 8); e += 256) {
+      const int c = e / BT, key = e % BT;
+      out[e] = *reinterpret_cast<const uint4*>(&tile[key * RW + c * 4]);
+    }
+  } else {
+    uint4* out = reinterpret_cast<uint4*>(vc + tile_off);
+    for (int e = threadIdx.x; e < D * (BT / 8); e += 256) {
+      const int c = e / D, d = e % D;
+      uint32_t w[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int k0 = vt_perm(c * 8 + 2 * x), k1 = vt_perm(c * 8 + 2 * x + 1);
+        const uint32_t lo = (tile[k0 * RW + (d >> 1)] >> ((d & 1) * 16)) & 0xffffu;
+        const uint32_t hi = (tile[k1 * RW + (d >> 1)] >> ((d & 1) * 16)) & 0xffffu;
+        w[x] = lo | (hi << 16);
+      }
+      out[e] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Work schedule: a stable LSD radix sort (4-bit digits, one workgroup) of the
+// rows by key.  NNZ_SORTED: key = nb - count (largest rows first).
+// HEAD_PHASED: key = phase * (nb + 1) + nb - count, phase = head / hpp.
+// Ties keep row order.  Also resets the persistent queue head.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned sched_key(const int* row_ptr, int r, int nb, int phased,
+                                              int hpp) {
+  const int cnt = row_ptr[r + 1] - row_ptr[r];
+  const unsigned k = (unsigned)(nb - cnt);
+  return phased ? (unsigned)((r / nb) / hpp) * (unsigned)(nb + 1) + k : k;
+}
+
+__global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restrict__ row_ptr,
+                                                       int mode, int hpp, int* __restrict__ sched,
+                                                       int* __restrict__ buf_a,
+                                                       int* __restrict__ buf_b,
+                                                       int* __restrict__ counter) {
+  constexpr int NT = 512;
+  __shared__ unsigned offs[16][NT];
+  __shared__ unsigned stmp[NT / 64 + 1];
+  const int rows = g.rows;
+  if (threadIdx.x == 0) counter[0] = 0;
+  if (mode == ABS_SCHED_HEAD_MAJOR) {
+    for (int r = threadIdx.x; r < rows; r += NT) sched[r] = r;
+    return;
+  }
+  const int phased = mode == ABS_SCHED_HEAD_PHASED;
+  const int nphase = phased ? (g.B * g.H + hpp - 1) / hpp : 1;
+  const unsigned maxkey = (unsigned)nphase * (unsigned)(g.nb + 1);
+  int passes = 1;
+  while (passes < 8 && (maxkey >> (4 * passes)) != 0u) ++passes;
+  const int per = (rows + NT - 1) / NT;
+  const int lo = threadIdx.x * per, hi = min(rows, lo + per);
+  for (int pass = 0; pass < passes; ++pass) {
+    const int* src = pass == 0 ? nullptr : ((pass & 1) ? buf_a : buf_b);
+    int* dst = pass == passes - 1 ? sched : ((pass & 1) ? buf_b : buf_a);
+    const int sh = 4 * pass;
+    unsigned cnt[16];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) cnt[x] = 0u;
+    for (int e = lo; e < hi; ++e) {
+      const int r = src ? src[e] : e;
+      const unsigned dg = (sched_key(row_ptr, r, g.nb, phased, hpp) >> sh) & 15u;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) cnt[x] += (dg == (unsigned)x) ? 1u : 0u;
+    }
+#pragma unroll
+    for (int x = 0; x < 16; ++x) offs[x][threadIdx.x] = cnt[x];
+    __syncthreads();
+    // exclusive scan of the flattened [digit][thread] table: thread t owns
+    // the 16 consecutive entries 16t .. 16t+15
+    unsigned loc[16];
+    unsigned run = 0u;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const int f = threadIdx.x * 16 + x;
+      loc[x] = run;
+      run += offs[f / NT][f % NT];
+    }
+    unsigned tot;
+    const unsigned pre = block_exclusive_scan<NT>(run, stmp, &tot);
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const int f = threadIdx.x * 16 + x;
+      offs[f / NT][f % NT] = pre + loc[x];
+    }
+    __syncthreads();
+    for (int e = lo; e < hi; ++e) {
+      const int r = src ? src[e] : e;
+      const unsigned dg = (sched_key(row_ptr, r, g.nb, phased, hpp) >> sh) & 15u;
+      const unsigned pos = offs[dg][threadIdx.x]++;
+      dst[pos] = r;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void reset_counter_kernel(int* counter) { counter[0] = 0; }
+
+// ---------------------------------------------------------------------------
+// bf16 block-sparse attention, one workgroup of BT/32 waves per item (query
+// block).  Wave w owns query slots 32w .. 32w+31.  Per kept key block j, in
+// chunks of 64 keys:
+//   S^T (keys x queries) = K_j Q^T with v_mfma_f32_32x32x16_bf16 (Q^T held in
+//     registers as the B operand, K_j read from LDS as the A operand);
+//   padding keys get -1e30 through one extra MFMA k-step (bias column times a
+//     ones row), so no per-element masking is needed;
+//   online softmax per query column: running max and sum in float32, exp2
+//     with log2(e)/sqrt(d) folded into one FMA;
+//   O^T (d x queries) += Vt_j P^T, the probabilities converted to bf16 straight
+//     from the accumulator layout (see vt_perm).
+// K_j and V_j arrive through direct global->LDS loads (global_load_lds_dwordx4)
+// of the chunk-major tiles; K_{j+1} is fetched while the softmax and PV of
+// block j run, V_{j+1} while the QK^T and softmax of block j+1 run.
+// PERSIST: workgroups pull items (sched order) from an atomic queue until it is
+// exhausted; otherwise one workgroup per item.
+// ---------------------------------------------------------------------------
+template <int D, int BT>
+struct AttnCfg {
+  static constexpr int NW = BT / 32, NT = 64 * NW;
+  static constexpr int TILE = BT * D * 2;            // bytes of one K or V tile
+  static constexpr int INSTR = TILE / 1024;          // 1 KB per wave-wide DMA
+  static constexpr int ROUNDS = INSTR / NW;          // DMAs per thread per tile
+  static constexpr int KS = D / 16, NSUB = BT / 32, DSUB = D / 32;
+  static constexpr int CHS = NSUB < 2 ? NSUB : 2;    // 32-key subtiles per softmax chunk
+  static constexpr int NCH = NSUB / CHS;
+  static_assert(ROUNDS * NW == INSTR, "tile split");
+};
+
+struct AttnArgs {
+  Geo g;
+  const bf16_t* q;
+  const bf16_t* kc;
+  const bf16_t* vc;
+  const int* row_ptr;
+  const int* col_idx;
+  const int* sched;
+  int* counter;
+  bf16_t* o;
+  long long* telem;
+  float c;  // log2(e) / sqrt(d)
+  int head_major;
+};
+
+typedef __attribute__((address_space(4))) const int cint_t;  // scalar-loadable
+__device__ __forceinline__ int ld_scalar(const int* p, long i) {
+  return ((cint_t*)(const void*)p)[i];
+}
+
+// Copy 16 bytes per lane from global memory into LDS at lds_base + 16*lane.
+// Written as inline asm so that the compiler does not treat the transfer as
+// an LDS store it must wait for before every LDS read; completion is tracked
+// explicitly with s_waitcnt vmcnt.  The instruction writes no registers.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
+template <int D, int BT, bool PERSIST>
+__global__ __launch_bounds__(2 * BT, 2) void attn_bf16_kernel(AttnArgs a) {
+  using C = AttnCfg<D, BT>;
+  __shared__ __attribute__((aligned(1024))) char sK[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char sV[C::TILE];
+  __shared__ int s_off[BT];
+  __shared__ int s_crd[BT];
+  __shared__ int s_item;
+
+  const Geo& g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, l32 = lane & 31;
+  for (int s = tid; s < BT; s += C::NT) {
+    const int plane = g.bh * g.bw;
+    const int st = s / plane, sh = (s / g.bw) % g.bh, sw = s % g.bw;
+    s_off[s] = (st * g.Hg + sh) * g.W + sw;
+    s_crd[s] = st | (sh << 8) | (sw << 16);
+  }
+  __syncthreads();
+
+  const uint32_t sK_base = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)sK;
+  const uint32_t sV_base = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)sV;
+  // per-lane LDS byte offsets of the MFMA A operands (see the re-layout)
+  const char* kread = sK + hf * (BT * 16) + l32 * 16;
+  const char* vread = sV + hf * (D * 16) + l32 * 16;
+  const long long t_start = (long long)wall_clock64();
+  long long tiles = 0;
+
+  int iter = 0;
+  while (true) {
+    int r;
+    if (PERSIST) {
+      if (tid == 0) s_item = atomicAdd(a.counter, 1);
+      __syncthreads();
+      const int it = __builtin_amdgcn_readfirstlane(s_item);
+      if (it >= g.rows) break;
+      r = ld_scalar(a.sched, it);
+    } else {
+      if (iter > 0) break;
+      r = a.head_major ? (int)blockIdx.x : ld_scalar(a.sched, blockIdx.x);
+    }
+    ++iter;
+    r = __builtin_amdgcn_readfirstlane(r);
+
+    const int bhh = r / g.nb, iq = r % g.nb;
+    const int b = bhh / g.H, h = bhh % g.H;
+    const long tok_base = (long)b * g.N;
+    const int rp0 = ld_scalar(a.row_ptr, r);
+    const int nnz = ld_scalar(a.row_ptr, r + 1) - rp0;
+    const int* cols = a.col_idx + rp0;
+    const char* kc_head = (const char*)(a.kc + (long)bhh * g.nb * (D * BT));
+    const char* vc_head = (const char*)(a.vc + (long)bhh * g.nb * (D * BT));
+
+    auto issue = [&](const char* tile_src, uint32_t lds) {
+#pragma unroll
+      for (int rr = 0; rr < C::ROUNDS; ++rr) {
+        const int inst = rr * C::NW + w;
+        dma16(tile_src + inst * 1024 + lane * 16, lds + inst * 1024);
+      }
+    };
+
+    int jn = ld_scalar(cols, 0);
+    issue(kc_head + (long)jn * C::TILE, sK_base);
+    issue(vc_head + (long)jn * C::TILE, sV_base);
+
+    // query block geometry and this lane's query slot
+    const int tq = iq / (g.nbh * g.nbw), hq = (iq / g.nbw) % g.nbh, wq = iq % g.nbw;
+    const int n0q = ((tq * g.bt) * g.Hg + hq * g.bh) * g.W + wq * g.bw;
+    const int TlQ = g.T - tq * g.bt, HlQ = g.Hg - hq * g.bh, WlQ = g.W - wq * g.bw;
+    const int qs = 32 * w + l32;
+    const int qcrd = s_crd[qs];
+    const bool qvalid =
+        (qcrd & 255) < TlQ && ((qcrd >> 8) & 255) < HlQ && ((qcrd >> 16) & 255) < WlQ;
+    const long nq = n0q + s_off[qs];
+
+    // Q^T as the B operand: lane holds 8 consecutive d of query slot qs
+    bf16x8_t qop[C::KS];
+    {
+      const bf16_t* qrow = a.q + ((tok_base + nq) * g.H + h) * D + 8 * hf;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (qvalid) v = *reinterpret_cast<const u32x4_t*>(qrow + 16 * ks);
+        qop[ks] = __builtin_bit_cast(bf16x8_t, v);
+      }
+      // Consume the Q registers here so that the compiler waits for their
+      // loads once per item and not at the top of every key-block iteration.
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) asm volatile("" ::"v"(qop[ks]));
+    }
+
+    f32x16_t o[C::DSUB];
+#pragma unroll
+    for (int u = 0; u < C::DSUB; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[u][e] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    for (int jj = 0; jj < nnz; ++jj) {
+      const int j = jn;
+      const bool more = jj + 1 < nnz;
+      jn = more ? ld_scalar(cols, jj + 1) : 0;
+      const int tb = j / (g.nbh * g.nbw), hb = (j / g.nbw) % g.nbh, wb = j % g.nbw;
+      const int Tl = g.T - tb * g.bt, Hl = g.Hg - hb * g.bh, Wl = g.W - wb * g.bw;
+      const bool partial = Tl < g.bt || Hl < g.bh || Wl < g.bw;
+
+      wait_vmcnt<C::ROUNDS>();       // this thread's K_j copies have landed
+      wg_barrier();                  // ... and every other thread's
+#pragma unroll
+      for (int hc = 0; hc < C::NCH; ++hc) {
+        // ---- S^T = K Q^T for the CHS key subtiles of this chunk
+        f32x16_t s[C::CHS];
+#pragma unroll
+        for (int t2 = 0; t2 < C::CHS; ++t2) {
+          const int t = hc * C::CHS + t2;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[t2][e] = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) {
+            const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(
+                kread + ks * (2 * BT * 16) + t * 512);
+            s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qop[ks], s[t2], 0, 0, 0);
+          }
+          if (partial) {
+            // padding keys: add -1e30 through one extra k-step (bias column x ones row)
+            const int crd = s_crd[32 * t + l32];
+            const bool ok =
+                (crd & 255) < Tl && ((crd >> 8) & 255) < Hl && ((crd >> 16) & 255) < Wl;
+            bf16x8_t bias, ones;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { bias[e] = (__bf16)0.0f; ones[e] = (__bf16)0.0f; }
+            if (hf == 0) ones[0] = (__bf16)1.0f;
+            if (hf == 0 && !ok) bias[0] = (__bf16)(-1.0e30f);
+            s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias, ones, s[t2], 0, 0, 0);
+          }
+        }
+        if (hc == C::NCH - 1) {
+          wg_barrier();              // every wave is done reading K_j
+          if (more) issue(kc_head + (long)jn * C::TILE, sK_base);
+        }
+
+        // ---- online softmax over the chunk's keys, per query column
+        float mt = -INFINITY;
+#pragma unroll
+        for (int t2 = 0; t2 < C::CHS; ++t2)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[t2][e]);
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_new = fmaxf(m_run, mt);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * a.c);
+        const float mc = m_use * a.c;
+        bf16x8_t pop[2 * C::CHS];
+        float psum = 0.f;
+#pragma unroll
+        for (int t2 = 0; t2 < C::CHS; ++t2)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[t2][e], a.c, -mc));
+            psum += pv;
+            pop[2 * t2 + e / 8][e % 8] = (__bf16)pv;
+          }
+        l_run = l_run * alpha + psum;
+        if (m_new != m_run) {
+#pragma unroll
+          for (int u = 0; u < C::DSUB; ++u)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[u][e] *= alpha;
+        }
+        m_run = m_new;
+
+        if (hc == 0) {
+          if (more) wait_vmcnt<C::ROUNDS>();   // V_j landed (K_{j+1} may be in flight)
+          else wait_vmcnt<0>();
+          wg_barrier();
+        }
+        // ---- O^T += Vt P^T over the chunk's keys
+#pragma unroll
+        for (int u = 0; u < C::DSUB; ++u) {
+#pragma unroll
+          for (int st2 = 0; st2 < 2 * C::CHS; ++st2) {
+            const int st = hc * 2 * C::CHS + st2;
+            const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(
+                vread + st * (2 * D * 16) + u * 512);
+            o[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pop[st2], o[u], 0, 0, 0);
+          }
+        }
+      }
+      wg_barrier();                  // every wave is done reading V_j
+      if (more) issue(vc_head + (long)jn * C::TILE, sV_base);
+    }
+    tiles += nnz;
+
+    // ---- epilogue: normalise and store the real query rows
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    if (qvalid) {
+      bf16_t* orow = a.o + ((tok_base + nq) * g.H + h) * D + 4 * hf;
+#pragma unroll
+      for (int u = 0; u < C::DSUB; ++u)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          __bf16 v0 = (__bf16)(o[u][4 * g4 + 0] * inv), v1 = (__bf16)(o[u][4 * g4 + 1] * inv);
+          __bf16 v2 = (__bf16)(o[u][4 * g4 + 2] * inv), v3 = (__bf16)(o[u][4 * g4 + 3] * inv);
+          const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
+          const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, v2) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
+          *reinterpret_cast<uint2*>(orow + 32 * u + 8 * g4) = make_uint2(w0, w1);
+        }
+    }
+    if (PERSIST) __syncthreads();  // s_item is rewritten by the next pull
+  }
+  if (tid == 0 && a.telem) {
+    long long* t = a.telem + (long)blockIdx.x * 4;
+    t[0] = (long long)hw_id_reg();
+    t[1] = (long long)xcc_id_reg();
+    t[2] = tiles;
+    t[3] = (long long)wall_clock64() - t_start;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 block-sparse attention (scalar FMA path, tiny and fp32 workloads):
+// one workgroup per item, one thread per query slot, keys in chunks of 32.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(128) void attn_f32_kernel(Geo g, const float* __restrict__ q,
+                                                       const float* __restrict__ k,
+                                                       const float* __restrict__ v,
+                                                       const int* __restrict__ row_ptr,
+                                                       const int* __restrict__ col_idx,
+                                                       const int* __restrict__ sched,
+                                                       int head_major, float* __restrict__ o,
+                                                       long long* __restrict__ telem,
+                                                       float scale) {
+  __shared__ float sk[32][D + 1];
+  __shared__ float sv[32][D];
+  __shared__ int kval[32];
+  const long long t_start = (long long)wall_clock64();
+  const int r = head_major ? (int)blockIdx.x : sched[blockIdx.x];
+  const int bhh = r / g.nb, iq = r % g.nb;
+  const int b = bhh / g.H, h = bhh % g.H;
+  const int plane = g.bh * g.bw;
+  auto tok = [&](int blk, int s, bool* ok) -> long {
+    const int tb = blk / (g.nbh * g.nbw), hb = (blk / g.nbw) % g.nbh, wb = blk % g.nbw;
+    const int st = s / plane, sh = (s / g.bw) % g.bh, sw = s % g.bw;
+    const int t = tb * g.bt + st, hh = hb * g.bh + sh, ww = wb * g.bw + sw;
+    *ok = t < g.T && hh < g.Hg && ww < g.W;
+    return ((long)t * g.Hg + hh) * g.W + ww;
+  };
+  const int qs = threadIdx.x;
+  bool qok = false;
+  long nq = 0;
+  if (qs < g.Bt) nq = tok(iq, qs, &qok);
+  float qv[D], acc[D];
+#pragma unroll
+  for (int x = 0; x < D; ++x) {
+    qv[x] = qok ? q[(((long)b * g.N + nq) * g.H + h) * D + x] * scale : 0.f;
+    acc[x] = 0.f;
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+  const int rp0 = row_ptr[r], rp1 = row_ptr[r + 1];
+  for (int jj = rp0; jj < rp1; ++jj) {
+    const int j = col_idx[jj];
+    for (int k0 = 0; k0 < g.Bt; k0 += 32) {
+      __syncthreads();
+      for (int e = threadIdx.x; e < 32 * D; e += 128) {
+        const int kk = e / D, x = e % D;
+        bool ok = false;
+        long n = 0;
+        if (k0 + kk < g.Bt) n = tok(j, k0 + kk, &ok);
+        const long off = (((long)b * g.N + n) * g.H + h) * D + x;
+        sk[kk][x] = ok ? k[off] : 0.f;
+        sv[kk][x] = ok ? v[off] : 0.f;
+        if (x == 0) kval[kk] = ok ? 1 : 0;
+      }
+      __syncthreads();
+      float sc[32];
+      float mt = -INFINITY;
+      for (int kk = 0; kk < 32; ++kk) {
+        float d = 0.f;
+#pragma unroll
+        for (int x = 0; x < D; ++x) d = fmaf(qv[x], sk[kk][x], d);
+        sc[kk] = kval[kk] ? d : -INFINITY;
+        mt = fmaxf(mt, sc[kk]);
+      }
+      const float m_new = fmaxf(m_run, mt);
+      if (m_new == -INFINITY) continue;
+      const float alpha = expf(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int x = 0; x < D; ++x) acc[x] *= alpha;
+      for (int kk = 0; kk < 32; ++kk) {
+        const float pw = expf(sc[kk] - m_new);
+        l_run += pw;
+#pragma unroll
+        for (int x = 0; x < D; ++x) acc[x] = fmaf(pw, sv[kk][x], acc[x]);
+      }
+      m_run = m_new;
+    }
+  }
+  if (qok) {
+    const float inv = 1.0f / l_run;
+#pragma unroll
+    for (int x = 0; x < D; ++x) o[(((long)b * g.N + nq) * g.H + h) * D + x] = acc[x] * inv;
+  }
+  if (threadIdx.x == 0 && telem) {
+    long long* t = telem + (long)blockIdx.x * 4;
+    t[0] = (long long)hw_id_reg();
+    t[1] = (long long)xcc_id_reg();
+    t[2] = rp1 - rp0;
+    t[3] = (long long)wall_clock64() - t_start;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <int D, int BT>
+static void launch_relayout(const Geo& g, const void* k, const void* v, bf16_t* kc, bf16_t* vc,
+                            hipStream_t s) {
+  hipLaunchKernelGGL((kv_relayout_kernel<D, BT>), dim3(g.nb, g.B * g.H, 2), dim3(256), 0, s, g,
+                     (const bf16_t*)k, (const bf16_t*)v, kc, vc);
+}
+
+hipError_t launch_attend_prepare(const Geo& g, int dtype, const void* k, const void* v,
+                                 const abs_mask* mask, int sched, int heads_per_phase, char* ws,
+                                 const AttendWs& L, hipStream_t s) {
+  if (dtype == ABS_BF16) {
+    bf16_t* kc = (bf16_t*)(ws + L.kc);
+    bf16_t* vc = (bf16_t*)(ws + L.vc);
+    if (g.d == 128) {
+      if (g.Bt == 128) launch_relayout<128, 128>(g, k, v, kc, vc, s);
+      else if (g.Bt == 64) launch_relayout<128, 64>(g, k, v, kc, vc, s);
+      else launch_relayout<128, 32>(g, k, v, kc, vc, s);
+    } else {
+      if (g.Bt == 128) launch_relayout<64, 128>(g, k, v, kc, vc, s);
+      else if (g.Bt == 64) launch_relayout<64, 64>(g, k, v, kc, vc, s);
+      else launch_relayout<64, 32>(g, k, v, kc, vc, s);
+    }
+  } else {
+    // float32 path: the attention kernel reads V token-major from the workspace
+    const size_t bytes = (size_t)g.B * g.N * g.H * g.d * sizeof(float);
+    hipError_t e = hipMemcpyAsync(ws + L.vc, v, bytes, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(512), 0, s, g, mask->row_ptr, sched,
+                     heads_per_phase, (int*)(ws + L.sched), (int*)(ws + L.sort_a),
+                     (int*)(ws + L.sort_b), (int*)(ws + L.counter));
+  return hipGetLastError();
+}
+
+template <int D, int BT, bool P>
+static const void* bf16_kernel_ptr() {
+  return reinterpret_cast<const void*>(&attn_bf16_kernel<D, BT, P>);
+}
+
+template <int D, int BT>
+static int persistent_grid() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  static int cache_cu[64] = {0};
+  static int cache_occ[64][6] = {{0}};
+  int cu = dev < 64 ? __atomic_load_n(&cache_cu[dev], __ATOMIC_RELAXED) : 0;
+  if (cu == 0) {
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    if (dev < 64) __atomic_store_n(&cache_cu[dev], cu, __ATOMIC_RELAXED);
+  }
+  const int slot = (D == 128 ? 0 : 3) + (BT == 128 ? 0 : (BT == 64 ? 1 : 2));
+  int occ = dev < 64 ? __atomic_load_n(&cache_occ[dev][slot], __ATOMIC_RELAXED) : 0;
+  if (occ == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &occ, reinterpret_cast<const void*>(&attn_bf16_kernel<D, BT, true>), 2 * BT, 0) !=
+            hipSuccess ||
+        occ < 1)
+      occ = 1;
+    if (dev < 64) __atomic_store_n(&cache_occ[dev][slot], occ, __ATOMIC_RELAXED);
+  }
+  return cu * occ;
+}
+
+int attend_grid(const Geo& g, int dtype, int sched) {
+  if (dtype != ABS_BF16 || sched == ABS_SCHED_HEAD_MAJOR) return g.rows;
+  if (g.d == 128) {
+    if (g.Bt == 128) return persistent_grid<128, 128>();
+    if (g.Bt == 64) return persistent_grid<128, 64>();
+    return persistent_grid<128, 32>();
+  }
+  if (g.Bt == 128) return persistent_grid<64, 128>();
+  if (g.Bt == 64) return persistent_grid<64, 64>();
+  return persistent_grid<64, 32>();
+}
+
+template <int D, int BT>
+static void launch_bf16(const AttnArgs& a, bool persist, int grid, hipStream_t s) {
+  if (persist)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, BT, true>), dim3(grid), dim3(2 * BT), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<D, BT, false>), dim3(grid), dim3(2 * BT), 0, s, a);
+}
+
+hipError_t launch_attend_run(const Geo& g, int dtype, const void* q, const void* k,
+                             const abs_mask* mask, void* o, int sched, char* ws,
+                             const AttendWs& L, int64_t* telemetry, int grid, hipStream_t s) {
+  const int* sch = (const int*)(ws + L.sched);
+  const bool head_major = sched == ABS_SCHED_HEAD_MAJOR;
+  if (dtype == ABS_BF16) {
+    AttnArgs a;
+    a.g = g;
+    a.q = (const bf16_t*)q;
+    a.kc = (const bf16_t*)(ws + L.kc);
+    a.vc = (const bf16_t*)(ws + L.vc);
+    a.row_ptr = mask->row_ptr;
+    a.col_idx = mask->col_idx;
+    a.sched = sch;
+    a.counter = (int*)(ws + L.counter);
+    a.o = (bf16_t*)o;
+    a.telem = (long long*)telemetry;
+    a.c = (float)(1.4426950408889634 / sqrt((double)g.d));
+    a.head_major = head_major ? 1 : 0;
+    const bool persist = !head_major;
+    if (persist) hipLaunchKernelGGL(reset_counter_kernel, dim3(1), dim3(1), 0, s, a.counter);
+    if (g.d == 128) {
+      if (g.Bt == 128) launch_bf16<128, 128>(a, persist, grid, s);
+      else if (g.Bt == 64) launch_bf16<128, 64>(a, persist, grid, s);
+      else launch_bf16<128, 32>(a, persist, grid, s);
+    } else {
+      if (g.Bt == 128) launch_bf16<64, 128>(a, persist, grid, s);
+      else if (g.Bt == 64) launch_bf16<64, 64>(a, persist, grid, s);
+      else launch_bf16<64, 32>(a, persist, grid, s);
+    }
+  } else {
+    const float scale = (float)(1.0 / sqrt((double)g.d));
+    if (g.d == 128)
+      hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(g.rows), dim3(128), 0, s, g, (const float*)q,
+                         (const float*)k, (const float*)(ws + L.vc), mask->row_ptr, mask->col_idx,
+                         sch, head_major ? 1 : 0, (float*)o, (long long*)telemetry, scale);
+    else
+      hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(g.rows), dim3(128), 0, s, g, (const float*)q,
+                         (const float*)k, (const float*)(ws + L.vc), mask->row_ptr, mask->col_idx,
+                         sch, head_major ? 1 : 0, (float*)o, (long long*)telemetry, scale);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace abs_impl

@@ -1,0 +1,64 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "abs.h"
+
+namespace abs_impl {
+
+// Block geometry passed by value to every kernel.
+struct Geo {
+  int B, H, d;
+  int T, Hg, W;        // real latent grid
+  int bt, bh, bw;      // block dims
+  int nbt, nbh, nbw;   // blocks per axis
+  int nb, Bt;          // blocks per head, tokens per block
+  int N;               // tokens
+  int rows;            // B*H*nb
+  int words;           // 32-bit words of one row bitmap, ceil(nb/32)
+};
+
+// Route workspace layout (byte offsets, all 256-aligned).
+struct RouteWs {
+  size_t qp, kp;          // float [B*H*nb*d] each
+  size_t score;           // float [rows*nb]: scores, then probabilities
+  size_t bitmap;          // uint32 [rows*words]
+  size_t count;           // int32 [rows]
+  size_t hist;            // uint32 [B*H*2048] slack radix histogram
+  size_t sel;             // int32 [B*H*4] slack selection state
+  size_t eqcnt, eqoff;    // int32 [rows] each
+  size_t total;
+};
+
+// Attend workspace layout.
+struct AttendWs {
+  size_t sched;           // int32 [rows]
+  size_t counter;         // int32 [64] queue head (+ padding)
+  size_t sort_a, sort_b;  // int32 [rows] each, radix-sort ping-pong
+  size_t kc, vc;          // bf16: chunk-major K and V block tiles [B*H*nb*Bt*d] each;
+                          // float32: vc holds a token-major copy of V, kc is empty
+  size_t total;
+};
+
+Geo make_geo(const abs_plan* plan);
+RouteWs route_ws_layout(const Geo& g, bool slack);
+AttendWs attend_ws_layout(const Geo& g, int dtype);
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_route(const Geo& g, int dtype, const void* q, const void* k, float p,
+                        int k_floor, float slack, const abs_mask* mask, char* ws,
+                        const RouteWs& L, hipStream_t s);
+hipError_t launch_attend_prepare(const Geo& g, int dtype, const void* k, const void* v,
+                                 const abs_mask* mask,
+                                 int sched, int heads_per_phase, char* ws, const AttendWs& L,
+                                 hipStream_t s);
+hipError_t launch_attend_run(const Geo& g, int dtype, const void* q, const void* k,
+                             const abs_mask* mask, void* o, int sched, char* ws,
+                             const AttendWs& L, int64_t* telemetry, int grid, hipStream_t s);
+int attend_grid(const Geo& g, int dtype, int sched);
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace abs_impl

@@ -1,0 +1,173 @@
+/*
+ * abs.h - C ABI of the adaptive block-sparse video attention library (MI355X,
+ * gfx950).  Plain pointers and sizes only; every device pointer is memory the
+ * caller owns (for instance torch tensors); the library never allocates, frees
+ * or synchronises, and launches all work asynchronously on the given stream.
+ *
+ * The method is the one described by the FVAttn explainer ("FVAttn: adaptive
+ * sparse attention with runtime load balancing, for video generation", an
+ * explainer of arXiv 2607.16190), section "Core method":
+ *   part 1, sparse-routing frontend: 3D video blocks, per-head Top-p routing
+ *           over a cheap approximate similarity, a Top-k safety floor, and a
+ *           repair of holes in the materialised mask;
+ *   part 2, runtime load balancing: measure each head's mask size before the
+ *           kernel runs and give the heaviest work out first (here: across the
+ *           compute units of one GPU instead of across ranks);
+ *   part 3, slack-aware augmentation: fill spare capacity with the highest
+ *           scoring blocks (here: a fixed per-head block budget).
+ *
+ * Tensor layout.  q, k, v and o are contiguous [B, N, H, d] with the N = T*H*W
+ * latent tokens in row-major (t, h, w) order, the layout a DiT's QKV projection
+ * emits.  Element type is float32 (ABS_F32) or bfloat16 (ABS_BF16); o has the
+ * type of q.  The softmax scale is 1/sqrt(d).
+ *
+ * Blocks.  Each axis of the latent grid is padded up to a whole number of
+ * (bt, bh, bw) blocks.  Block index ((t/bt)*nbh + h/bh)*nbw + w/bw and slot
+ * ((t%bt)*bh + h%bh)*bw + w%bw are row-major at both levels; query and key
+ * blocks share this blocking.  Padding tokens do not exist: they are excluded
+ * from the pooled means, masked as keys and produce no output.
+ *
+ * Errors.  Every entry point validates its arguments on the host before any
+ * launch and returns ABS_EINVAL / ABS_ENOTSUP / ABS_ENOSPACE without touching
+ * the device.  ABS_EHIP reports a launch error from the HIP runtime.  Nothing
+ * throws across this interface.  Calls on distinct streams with distinct
+ * workspaces are independent (the library holds no mutable global state apart
+ * from a per-device cache of the compute-unit count).
+ */
+#ifndef ABS_H
+#define ABS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ABS_OK = 0,
+  ABS_EINVAL = 1,   /* null pointer, non-positive size, p outside (0,1], ... */
+  ABS_ENOTSUP = 2,  /* head_dim, block size, dtype or size outside the built kernels */
+  ABS_ENOSPACE = 3, /* workspace smaller than the plan requires */
+  ABS_EHIP = 4      /* HIP launch error */
+} abs_status;
+
+typedef enum { ABS_F32 = 0, ABS_BF16 = 1 } abs_dtype;
+
+/* Order in which (batch, head, query-block) items are processed by attend.
+ *   NNZ_SORTED : persistent workgroups pull items from one queue sorted by the
+ *                row's kept-block count, largest first, ties by row index
+ *                (load balancing of the explainer's "Core method" part 2,
+ *                recast over compute units);
+ *   HEAD_MAJOR : one workgroup per item in natural (b, h, i) order, scheduled
+ *                by the hardware dispatcher (the unbalanced baseline);
+ *   HEAD_PHASED: persistent queue; heads are taken in phases of a few heads
+ *                (so their K/V stay cache resident), largest rows first inside
+ *                a phase, ties by row index.
+ * All three give bitwise identical outputs: every row has one owner and a
+ * fixed key-block order. */
+typedef enum {
+  ABS_SCHED_NNZ_SORTED = 0,
+  ABS_SCHED_HEAD_MAJOR = 1,
+  ABS_SCHED_HEAD_PHASED = 2
+} abs_sched;
+
+typedef struct {
+  int32_t batch, heads, head_dim;
+  int32_t grid[3];  /* T, H, W latent grid */
+  int32_t block[3]; /* bt, bh, bw */
+  int32_t dtype;    /* abs_dtype */
+} abs_shape;
+
+/* Host-side plan, filled by abs_plan_init.  Read-only afterwards. */
+typedef struct {
+  abs_shape s;
+  int32_t padded[3];       /* grid rounded up to whole blocks */
+  int32_t nblk[3];         /* blocks per axis */
+  int32_t num_blocks;      /* nb, blocks per head */
+  int32_t block_tokens;    /* Bt = bt*bh*bw */
+  int32_t heads_per_phase; /* phase width used by ABS_SCHED_HEAD_PHASED */
+  int32_t reserved;
+  int64_t tokens;          /* N = T*H*W */
+  int64_t rows;            /* B*H*nb rows of the block mask */
+  int64_t col_capacity;    /* rows*nb: worst-case col_idx length */
+  size_t route_ws_bytes;   /* workspace abs_route needs */
+  size_t attend_ws_bytes;  /* workspace abs_attend needs */
+} abs_plan;
+
+/* Per-head CSR block mask, device buffers owned by the caller:
+ *   row_ptr  int32 [rows + 1]       rows r = (b*H + h)*nb + i
+ *   col_idx  int32 [col_capacity]   kept key blocks of row r, ascending, in
+ *                                   col_idx[row_ptr[r] .. row_ptr[r+1])
+ *   head_nnz int32 [B*H]            kept blocks per head                   */
+typedef struct {
+  int32_t* row_ptr;
+  int32_t* col_idx;
+  int32_t* head_nnz;
+} abs_mask;
+
+/* Fill *out for the given shape.  Host only, synchronous, no device access.
+ * Supported: head_dim in {64, 128}; bt*bh*bw in {32, 64, 128}; nb <= 4096;
+ * rows*nb < 2^31. */
+abs_status abs_plan_init(const abs_shape* shape, abs_plan* out);
+
+/* Routing (explainer "Core method" part 1, and part 3 when slack > 0).
+ * For every row (b, h, i): Qp_i, Kp_j = means of q, k over the real tokens of
+ * block i, j; P_ij = softmax_j(Qp_i . Kp_j / sqrt(d)) in float32; blocks
+ * ordered by P descending (ties: lower j first); m = smallest count whose
+ * cumulative mass reaches p (>= p; p == 1 keeps all); keep the first
+ * min(nb, max(m, k_floor)) blocks plus block i itself.  With slack > 0 every
+ * head is then topped up to ceil(slack * nb^2) kept pairs with its unkept
+ * pairs of largest P (ties: lowest i*nb + j).  Writes the CSR into *mask.
+ *   q, k   : device [B, N, H, d] of the plan's dtype
+ *   p      : in (0, 1];  k_floor >= 1 (values above nb keep every block)
+ *   slack  : in [0, 1), 0 disables the fill
+ *   ws     : device workspace of at least plan->route_ws_bytes bytes.  On
+ *            return (stream order) it starts with the pooled means, float32
+ *            Qp [B, H, nb, d] followed by Kp [B, H, nb, d].
+ *   stream : hipStream_t (NULL = default stream)                         */
+abs_status abs_route(const abs_plan* plan, const void* q, const void* k, float p,
+                     int32_t k_floor, float slack, const abs_mask* mask, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Attention prologue: re-lays k and v block-major for the attention kernel
+ * (bf16) and builds the item order of `sched` from the mask's row lengths
+ * (explainer "Core method" part 2: profile the mask size per head, heaviest
+ * first).  On return (stream order) the workspace starts with that order,
+ * int32 [rows].
+ *   k, v : device [B, N, H, d] of the plan's dtype
+ *   ws   : device workspace of at least plan->attend_ws_bytes bytes; it must
+ *          be passed unchanged to abs_attend_run.                          */
+abs_status abs_attend_prepare(const abs_plan* plan, const void* k, const void* v,
+                              const abs_mask* mask, int32_t sched, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* Block-sparse attention over the kept blocks (explainer "Core method" part 1
+ * and "The real problem"): for each real query token of block i, one softmax
+ * over the real keys of all kept blocks of row (b, h, i), scale 1/sqrt(d),
+ * output written to o [B, N, H, d].  Requires abs_attend_prepare on the same
+ * ws, mask and sched earlier in stream order.
+ *   telemetry : NULL, or device int64 [abs_attend_grid(...) * 4]: per
+ *               workgroup {hardware id register, XCC id, kept tiles processed,
+ *               busy clock ticks}.                                          */
+abs_status abs_attend_run(const abs_plan* plan, const void* q, const void* k,
+                          const abs_mask* mask, void* o, int32_t sched, void* ws,
+                          size_t ws_bytes, int64_t* telemetry, void* stream);
+
+/* abs_attend_prepare followed by abs_attend_run. */
+abs_status abs_attend(const abs_plan* plan, const void* q, const void* k, const void* v,
+                      const abs_mask* mask, void* o, int32_t sched, void* ws,
+                      size_t ws_bytes, int64_t* telemetry, void* stream);
+
+/* Number of workgroups abs_attend_run launches for this plan and schedule on
+ * the current device (the telemetry record count).  Host query. */
+abs_status abs_attend_grid(const abs_plan* plan, int32_t sched, int32_t* workgroups);
+
+/* Static description of a status code. */
+const char* abs_status_string(abs_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ABS_H */

@@ -1,0 +1,124 @@
+"""Comparison helpers for the GPU parity tests (test code; uses the oracle)."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import oracle as O
+
+# Output tolerances: bf16 workloads max |d| <= 2e-2 and mean |d| <= 2e-3;
+# float32 workload max |d| <= 1e-4 (oracle attention fed the GPU's own mask).
+TOL_BF16_MAX, TOL_BF16_MEAN, TOL_F32_MAX = 2e-2, 2e-3, 1e-4
+
+
+def compare_masks(gpu_keep: np.ndarray, res: dict, p: float, k_floor: int, key: str = "keep"):
+    """Row-by-row comparison of a GPU mask with the oracle's.
+
+    Rows outside the float32 exemption rule (oracle.row_exemptions) must match
+    exactly.  Exempt rows must keep the own block, at least min(k_floor, nb)
+    blocks, mass >= p - 1e-4 (oracle P), a size within 1 of the oracle's and a
+    symmetric difference of at most 2 blocks.
+    Returns a dict of counts; raises AssertionError on any violation.
+    """
+    ref = res[key]
+    B, H, nb, _ = ref.shape
+    P = res["P"]
+    exempt = O.row_exemptions(res["diag"], p, k_floor)
+    exact_rows = mism = ex_ok = 0
+    bad = []
+    for b in range(B):
+        for h in range(H):
+            eq = (gpu_keep[b, h] == ref[b, h]).all(axis=1)
+            for i in range(nb):
+                if not exempt[b, h, i]:
+                    if eq[i]:
+                        exact_rows += 1
+                    else:
+                        mism += 1
+                        if len(bad) < 5:
+                            bad.append((b, h, i, np.nonzero(gpu_keep[b, h, i] != ref[b, h, i])[0]))
+                    continue
+                g = gpu_keep[b, h, i]
+                kept = int(g.sum())
+                assert g[i], (b, h, i, "own block missing")
+                assert kept >= min(k_floor, nb), (b, h, i, kept)
+                if p < 1.0:
+                    assert P[b, h, i][g].sum() >= p - 1e-4, (b, h, i)
+                assert abs(kept - int(ref[b, h, i].sum())) <= 1, (b, h, i)
+                assert int((g != ref[b, h, i]).sum()) <= 2, (b, h, i)
+                ex_ok += 1
+    assert mism == 0, f"{mism} non-exempt rows differ, e.g. {bad}"
+    return dict(exact=exact_rows, exempt=ex_ok, mismatched=mism)
+
+
+def check_slack(gpu_keep: np.ndarray, gpu_base: np.ndarray, P: np.ndarray, slack: float,
+                tie_rel: float = 1e-5):
+    """GPU slack fill against the oracle fill applied to the GPU's own base mask.
+
+    Pairs chosen differently may only be pairs whose probability is within a
+    relative 1e-5 of the head's selection threshold (float32 versus float64
+    probabilities).  Every head must hold exactly max(base, budget) pairs.
+    """
+    ref, info = O.slack_fill(P, gpu_base, slack)
+    B, H, nb, _ = P.shape
+    budget = int(math.ceil(float(slack) * nb * nb))
+    diffs = 0
+    for b in range(B):
+        for h in range(H):
+            g, r = gpu_keep[b, h], ref[b, h]
+            assert int(g.sum()) == max(int(gpu_base[b, h].sum()), budget), (b, h)
+            assert (g[gpu_base[b, h]]).all(), (b, h, "base pair dropped")
+            d = g != r
+            if d.any():
+                thr = info[(b, h)]["last"]
+                near = np.abs(P[b, h][d] - thr) <= tie_rel * thr
+                assert near.all(), (b, h, int(d.sum()), P[b, h][d][~near][:4], thr)
+                diffs += int(d.sum())
+    return diffs
+
+
+def sample_rows(row_ptr: np.ndarray, B: int, H: int, nb: int, geo, n_heads=8, n_blocks=16,
+                seed=0):
+    """Seeded sample of rows: n_heads heads (always the heaviest and lightest)
+    x n_blocks query blocks (always the heaviest row of the head and one
+    partially padded block)."""
+    rng = np.random.default_rng(seed)
+    counts = np.diff(row_ptr).reshape(B * H, nb)
+    head_nnz = counts.sum(axis=1)
+    heads = {int(head_nnz.argmax()), int(head_nnz.argmin())}
+    others = [x for x in range(B * H) if x not in heads]
+    rng.shuffle(others)
+    heads |= set(others[: max(0, n_heads - len(heads))])
+    members = O.block_members(geo)
+    partial = [i for i in range(nb) if (members[i] < 0).any()]
+    rows = []
+    for bh in sorted(heads):
+        blocks = {int(counts[bh].argmax())}
+        if partial:
+            blocks.add(int(rng.choice(partial)))
+        rest = [i for i in range(nb) if i not in blocks]
+        rng.shuffle(rest)
+        blocks |= set(rest[: max(0, n_blocks - len(blocks))])
+        rows += [bh * nb + i for i in sorted(blocks)]
+    return rows
+
+
+def compare_outputs(o_gpu: np.ndarray, o_ref: np.ndarray, geo, rows, H: int, dtype: str):
+    """Compare outputs of the real query tokens of the given rows."""
+    members = O.block_members(geo)
+    nb = geo.nb
+    errs = []
+    for r in rows:
+        bh, i = divmod(int(r), nb)
+        b, h = divmod(bh, H)
+        tok = members[i][members[i] >= 0]
+        errs.append(np.abs(o_gpu[b, tok, h, :].astype(np.float64) - o_ref[b, tok, h, :]).ravel())
+    e = np.concatenate(errs)
+    assert np.isfinite(e).all()
+    if dtype == "f32":
+        assert e.max() <= TOL_F32_MAX, e.max()
+    else:
+        assert e.max() <= TOL_BF16_MAX, e.max()
+        assert e.mean() <= TOL_BF16_MEAN, e.mean()
+    return float(e.max()), float(e.mean())

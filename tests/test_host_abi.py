@@ -1,0 +1,127 @@
+"""The C ABI on the host: the library loads, exports what the header declares,
+and rejects bad arguments before touching a device (runs without a GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import adaptive_block_sparse_amd as A
+import oracle as O
+import synth_inputs as si
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: validation fails first
+
+
+def _lib():
+    if not os.path.exists(A.LIB_PATH):
+        pytest.skip("libabs.so not built")
+    return A.load_library()
+
+
+def test_exports_match_header():
+    lib = _lib()
+    header = open(os.path.join(ROOT, "include", "abs.h")).read()
+    declared = set(re.findall(r"^\s*(?:abs_status|const char\*)\s+(abs_\w+)\s*\(", header, re.M))
+    assert declared == set(A.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name)
+    assert A.status_string(A.ENOSPACE) == "workspace too small"
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_plan_matches_geometry(cfg):
+    _lib()
+    wl = si.WORKLOADS[cfg]
+    plan = A.plan_init(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.block, wl.dtype)
+    geo = O.geometry(wl.grid, wl.block)
+    assert plan.num_blocks == geo.nb
+    assert tuple(plan.padded) == geo.padded and tuple(plan.nblk) == geo.nblk
+    assert plan.block_tokens == geo.bt_tokens
+    assert plan.rows == wl.batch * wl.heads * geo.nb
+    assert plan.col_capacity == plan.rows * geo.nb
+    assert plan.tokens == wl.tokens
+    assert plan.route_ws_bytes > 0 and plan.attend_ws_bytes > 0
+    assert A.attend_grid(plan, A.SCHED_HEAD_MAJOR) == plan.rows
+
+
+def _status_of_plan(**kw):
+    lib = _lib()
+    args = dict(batch=1, heads=2, head_dim=64, grid=(4, 8, 8), block=(2, 4, 4), dtype=A.F32)
+    args.update(kw)
+    shape = A.Shape(args["batch"], args["heads"], args["head_dim"],
+                    (ctypes.c_int32 * 3)(*args["grid"]), (ctypes.c_int32 * 3)(*args["block"]),
+                    args["dtype"])
+    plan = A.Plan()
+    return lib.abs_plan_init(ctypes.byref(shape), ctypes.byref(plan)), plan
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(), A.OK),
+    (dict(batch=0), A.EINVAL),
+    (dict(heads=-1), A.EINVAL),
+    (dict(grid=(0, 8, 8)), A.EINVAL),
+    (dict(block=(2, 0, 4)), A.EINVAL),
+    (dict(head_dim=96), A.ENOTSUP),
+    (dict(block=(2, 4, 6)), A.ENOTSUP),        # 48 tokens per block
+    (dict(dtype=7), A.ENOTSUP),
+    (dict(grid=(200, 200, 200), block=(2, 4, 4)), A.ENOTSUP),   # nb > 4096
+])
+def test_plan_validation(kw, want):
+    st, _ = _status_of_plan(**kw)
+    assert st == want
+
+
+def _plan(dtype=A.BF16):
+    st, plan = _status_of_plan(head_dim=128, grid=(21, 30, 52), block=(2, 8, 8), heads=4,
+                               dtype=dtype)
+    assert st == A.OK
+    return plan
+
+
+def _route(plan, q=FAKE, k=FAKE, p=0.9, kf=4, slack=0.0, ws_bytes=None, mask=True, ws=FAKE):
+    lib = _lib()
+    cm = A.CMask(0x100000, 0x200000, 0x300000)
+    ws_bytes = plan.route_ws_bytes if ws_bytes is None else ws_bytes
+    return lib.abs_route(ctypes.byref(plan), q, k, p, kf, slack,
+                         ctypes.byref(cm) if mask else None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(p=0.0), A.EINVAL), (dict(p=1.5), A.EINVAL), (dict(p=math.nan), A.EINVAL),
+    (dict(p=-0.1), A.EINVAL), (dict(kf=0), A.EINVAL), (dict(slack=1.0), A.EINVAL),
+    (dict(slack=-0.5), A.EINVAL), (dict(q=None), A.EINVAL), (dict(mask=False), A.EINVAL),
+    (dict(ws=None), A.EINVAL), (dict(ws_bytes=1024), A.ENOSPACE),
+])
+def test_route_validation(kw, want):
+    assert _route(_plan(), **kw) == want
+
+
+def test_route_slack_needs_its_scratch():
+    plan = _plan()
+    # without the fill the workspace may be smaller than the planned maximum
+    lib = _lib()
+    assert _route(plan, slack=0.15, ws_bytes=plan.route_ws_bytes - 4096) == A.ENOSPACE
+
+
+@pytest.mark.parametrize("sched,ws_small,want", [(5, False, A.EINVAL), (-1, False, A.EINVAL),
+                                                 (A.SCHED_NNZ_SORTED, True, A.ENOSPACE)])
+def test_attend_validation(sched, ws_small, want):
+    lib = _lib()
+    plan = _plan()
+    cm = A.CMask(0x100000, 0x200000, 0x300000)
+    nbytes = 1024 if ws_small else plan.attend_ws_bytes
+    st = lib.abs_attend_prepare(ctypes.byref(plan), FAKE, FAKE, ctypes.byref(cm), sched, FAKE,
+                                nbytes, None)
+    assert st == want
+    st = lib.abs_attend_run(ctypes.byref(plan), FAKE, FAKE, ctypes.byref(cm), FAKE, sched, FAKE,
+                            nbytes, None, None)
+    assert st == want
+    n = ctypes.c_int32()
+    if sched not in (0, 1, 2):
+        assert lib.abs_attend_grid(ctypes.byref(plan), sched, ctypes.byref(n)) == A.EINVAL
+    st = lib.abs_attend(ctypes.byref(plan), None, FAKE, FAKE, ctypes.byref(cm), FAKE, 0, FAKE,
+                        plan.attend_ws_bytes, None, None)
+    assert st == A.EINVAL
