@@ -295,18 +295,44 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_bf16_kernel(AttnArgs a) {
     const char* kc_head = (const char*)(a.kc + (long)bhh * g.nb * (D * BT));
     const char* vc_head = (const char*)(a.vc + (long)bhh * g.nb * (D * BT));
 
-    auto issue = [&](const char* tile_src, uint32_t lds) {
+    // A tile is copied in NCH parts (key halves when NCH == 2), G copies per
+    // thread each.  K part h: chunk j, keys [h*BT/2, (h+1)*BT/2); V part h:
+    // key positions [h*BT/2, (h+1)*BT/2), i.e. a contiguous TILE/NCH bytes.
+    constexpr int G = C::ROUNDS / C::NCH;
+    auto issue_k = [&](int jblk, int part) {
+      const char* src = kc_head + (long)jblk * C::TILE;
 #pragma unroll
-      for (int rr = 0; rr < C::ROUNDS; ++rr) {
-        const int inst = rr * C::NW + w;
-        dma16(tile_src + inst * 1024 + lane * 16, lds + inst * 1024);
+      for (int rr = 0; rr < G; ++rr) {
+        const int jx = rr * C::NW + w;
+        const int off = C::NCH == 1 ? jx * 1024 : jx * (BT * 16) + part * (BT * 8);
+        dma16(src + off + lane * 16, sK_base + off);
+      }
+    };
+    auto issue_v = [&](int jblk, int part) {
+      const char* src = vc_head + (long)jblk * C::TILE;
+#pragma unroll
+      for (int rr = 0; rr < G; ++rr) {
+        const int off = part * (C::TILE / C::NCH) + (rr * C::NW + w) * 1024;
+        dma16(src + off + lane * 16, sV_base + off);
       }
     };
 
+    // Issue order (NCH == 2), one group = G copies per thread:
+    //   K0_j, V0_j, K1_j   (prologue for j = first, else during block j-1)
+    //   V1_j               (top of half 0 of block j)
+    //   K0_{j+1}           (middle of half 0, once every wave has read K0_j)
+    //   V0_{j+1}           (top of half 1, once every wave has read V0_j)
+    //   K1_{j+1}           (middle of half 1)
+    // so each wait below names exactly how many groups were issued after the
+    // awaited one.  NCH == 1: K_j before block j, V_j at its top.
     int jn = ld_scalar(cols, 0);
-    issue(kc_head + (long)jn * C::TILE, sK_base);
-    issue(vc_head + (long)jn * C::TILE, sV_base);
-
+    if (C::NCH == 2) {
+      issue_k(jn, 0);
+      issue_v(jn, 0);
+      issue_k(jn, 1);
+    } else {
+      issue_k(jn, 0);
+    }
     // query block geometry and this lane's query slot
     const int tq = iq / (g.nbh * g.nbw), hq = (iq / g.nbw) % g.nbh, wq = iq % g.nbw;
     const int n0q = ((tq * g.bt) * g.Hg + hq * g.bh) * g.W + wq * g.bw;
@@ -348,11 +374,25 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_bf16_kernel(AttnArgs a) {
       const int Tl = g.T - tb * g.bt, Hl = g.Hg - hb * g.bh, Wl = g.W - wb * g.bw;
       const bool partial = Tl < g.bt || Hl < g.bh || Wl < g.bw;
 
-      wait_vmcnt<C::ROUNDS>();       // this thread's K_j copies have landed
-      wg_barrier();                  // ... and every other thread's
 #pragma unroll
       for (int hc = 0; hc < C::NCH; ++hc) {
-        // ---- S^T = K Q^T for the CHS key subtiles of this chunk
+        // ---- top: K part hc of block j has landed; V part (hc-1) is free
+        if (C::NCH == 2) {
+          if (hc == 0) wait_vmcnt<2 * G>();
+          else if (more) wait_vmcnt<2 * G>();
+          else wait_vmcnt<G>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        wg_barrier();
+        if (C::NCH == 2) {
+          if (hc == 0) issue_v(j, 1);
+          else if (more) issue_v(jn, 0);
+        } else {
+          issue_v(j, 0);
+        }
+
+        // ---- S^T = K Q^T for the CHS key subtiles of this part
         f32x16_t s[C::CHS];
 #pragma unroll
         for (int t2 = 0; t2 < C::CHS; ++t2) {
@@ -378,12 +418,19 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_bf16_kernel(AttnArgs a) {
             s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias, ones, s[t2], 0, 0, 0);
           }
         }
-        if (hc == C::NCH - 1) {
-          wg_barrier();              // every wave is done reading K_j
-          if (more) issue(kc_head + (long)jn * C::TILE, sK_base);
-        }
 
-        // ---- online softmax over the chunk's keys, per query column
+        // ---- middle: V part hc has landed; every wave is done with K part hc
+        if (C::NCH == 2) {
+          if (hc == 0) wait_vmcnt<2 * G>();
+          else if (more) wait_vmcnt<2 * G>();
+          else wait_vmcnt<0>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        wg_barrier();
+        if (more) issue_k(jn, hc);
+
+        // ---- online softmax over the part's keys, per query column
         float mt = -INFINITY;
 #pragma unroll
         for (int t2 = 0; t2 < C::CHS; ++t2)
@@ -413,12 +460,7 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_bf16_kernel(AttnArgs a) {
         }
         m_run = m_new;
 
-        if (hc == 0) {
-          if (more) wait_vmcnt<C::ROUNDS>();   // V_j landed (K_{j+1} may be in flight)
-          else wait_vmcnt<0>();
-          wg_barrier();
-        }
-        // ---- O^T += Vt P^T over the chunk's keys
+        // ---- O^T += Vt P^T over the part's keys
 #pragma unroll
         for (int u = 0; u < C::DSUB; ++u) {
 #pragma unroll
@@ -430,8 +472,6 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_bf16_kernel(AttnArgs a) {
           }
         }
       }
-      wg_barrier();                  // every wave is done reading V_j
-      if (more) issue(vc_head + (long)jn * C::TILE, sV_base);
     }
     tiles += nnz;
 

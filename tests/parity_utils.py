@@ -25,7 +25,7 @@ def compare_masks(gpu_keep: np.ndarray, res: dict, p: float, k_floor: int, key: 
     B, H, nb, _ = ref.shape
     P = res["P"]
     exempt = O.row_exemptions(res["diag"], p, k_floor)
-    exact_rows = mism = ex_ok = 0
+    exact_rows = mism = ex_ok = ex_equal = 0
     bad = []
     for b in range(B):
         for h in range(H):
@@ -48,8 +48,9 @@ def compare_masks(gpu_keep: np.ndarray, res: dict, p: float, k_floor: int, key: 
                 assert abs(kept - int(ref[b, h, i].sum())) <= 1, (b, h, i)
                 assert int((g != ref[b, h, i]).sum()) <= 2, (b, h, i)
                 ex_ok += 1
+                ex_equal += int(eq[i])
     assert mism == 0, f"{mism} non-exempt rows differ, e.g. {bad}"
-    return dict(exact=exact_rows, exempt=ex_ok, mismatched=mism)
+    return dict(exact=exact_rows, exempt=ex_ok, exempt_but_equal=ex_equal, mismatched=mism)
 
 
 def check_slack(gpu_keep: np.ndarray, gpu_base: np.ndarray, P: np.ndarray, slack: float,

@@ -105,6 +105,55 @@ def test_floor_above_nb_and_single_block():
     compare_outputs(r["o"], o_ref, O.geometry(one.grid, one.block), [0, 1], 2, "bf16")
 
 
+@pytest.mark.parametrize("p,slack", [(0.3, 0.5), (0.5, 0.7), (0.2, 0.97)])
+def test_slack_fill_active(p, slack):
+    """Heads below the budget: the fill must add exactly the oracle's pairs
+    (up to float32 near-ties at the threshold)."""
+    wl = SMALL["bf16-d128-bt128-ragged"]
+    p = float(np.float32(p))
+    inputs = si.make_inputs(wl)
+    geo = O.geometry(wl.grid, wl.block)
+    base = _run(wl, p, 1, inputs=inputs)
+    r = _run(wl, p, 1, slack=slack, inputs=inputs)
+    brp, bci = base["mask"].to_host()
+    rp, ci = r["mask"].to_host()
+    base_keep = O.csr_to_keep(brp, bci, 1, wl.heads, geo.nb)
+    keep = O.csr_to_keep(rp, ci, 1, wl.heads, geo.nb)
+    res = O.route(_np(inputs[0]), _np(inputs[1]), geo, p, 1)
+    compare_masks(base_keep, res, p, 1)
+    budget = int(np.ceil(np.float64(np.float32(slack)) * geo.nb ** 2))
+    assert (base_keep.reshape(wl.heads, -1).sum(1) < budget).any()      # the fill is active
+    print("slack pairs off the oracle", check_slack(keep, base_keep, res["P"], np.float32(slack)))
+    o_ref = O.sparse_attention(_np(inputs[0]), _np(inputs[1]), _np(inputs[2]), geo, rp, ci)
+    compare_outputs(r["o"], o_ref, geo, range(wl.heads * geo.nb), wl.heads, wl.dtype)
+
+
+@pytest.mark.slow
+def test_slack_fill_active_long_horizon():
+    """The long-horizon shape at p = 0.3 so that heads fall below the 15 %
+    budget; full mask check, sampled outputs."""
+    wl = si.WORKLOADS[4]
+    p = float(np.float32(0.3))
+    inputs = si.make_inputs(wl)
+    geo = O.geometry(wl.grid, wl.block)
+    base = _run(wl, p, wl.k_floor, inputs=inputs)
+    r = _run(wl, p, wl.k_floor, slack=wl.slack, inputs=inputs, telemetry=True)
+    brp, bci = base["mask"].to_host()
+    rp, ci = r["mask"].to_host()
+    base_keep = O.csr_to_keep(brp, bci, 1, wl.heads, geo.nb)
+    keep = O.csr_to_keep(rp, ci, 1, wl.heads, geo.nb)
+    q, k, v = (_np(t) for t in inputs)
+    res = O.route(q, k, geo, p, wl.k_floor)
+    print("base mask rows", compare_masks(base_keep, res, p, wl.k_floor))
+    dens = base_keep.reshape(wl.heads, -1).mean(1)
+    print("base density per head", np.round(dens, 3))
+    print("slack pairs off the oracle", check_slack(keep, base_keep, res["P"], np.float32(wl.slack)))
+    assert r["tel"][:, 2].sum() == ci.size
+    rows = sample_rows(rp, 1, wl.heads, geo.nb, geo, seed=44)
+    o_ref = O.sparse_attention(q, k, v, geo, rp, ci, rows=rows)
+    print("max/mean err", compare_outputs(r["o"], o_ref, geo, rows, wl.heads, wl.dtype))
+
+
 def test_schedules_are_bitwise_identical():
     wl = SMALL["bf16-d128-bt128-ragged"]
     inputs = si.make_inputs(wl)
