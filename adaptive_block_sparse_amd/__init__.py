@@ -20,7 +20,7 @@ import os
 from typing import Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libabs.so")
+LIB_PATH = os.environ.get("ABS_LIBRARY") or os.path.join(HERE, "libabs.so")
 
 OK, EINVAL, ENOTSUP, ENOSPACE, EHIP = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1

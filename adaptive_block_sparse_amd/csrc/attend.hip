@@ -101,16 +101,29 @@ __global__ __launch_bounds__(256) void kv_relayout_kernel(Geo g, const bf16_t* _
 }
 
 // ---------------------------------------------------------------------------
-// Work schedule: a stable LSD radix sort (4-bit digits, one workgroup) of the
-// rows by key.  NNZ_SORTED: key = nb - count (largest rows first).
-// HEAD_PHASED: key = phase * (nb + 1) + nb - count, phase = head / hpp.
-// Ties keep row order.  Also resets the persistent queue head.
+// Work schedule over attention work items (groups of one or two paired query
+// blocks of one head, see group_blocks).  A stable LSD radix sort (4-bit
+// digits, one workgroup) by key:
+//   NNZ_SORTED : key = 2nb - cost (largest first);
+//   HEAD_PHASED: key = phase * (2nb + 1) + 2nb - cost, phase = head / hpp;
+//   HEAD_MAJOR : natural order.
+// cost = kept blocks of the group's rows.  Ties keep item order.  Also resets
+// the persistent queue head.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ unsigned sched_key(const int* row_ptr, int r, int nb, int phased,
-                                              int hpp) {
-  const int cnt = row_ptr[r + 1] - row_ptr[r];
-  const unsigned k = (unsigned)(nb - cnt);
-  return phased ? (unsigned)((r / nb) / hpp) * (unsigned)(nb + 1) + k : k;
+__device__ __forceinline__ int group_cost(const Geo& g, const int* row_ptr, int item) {
+  const int bh = item / g.groups_per_head, gl = item % g.groups_per_head;
+  int lead, partner;
+  group_blocks(g, gl, &lead, &partner);
+  const int r = bh * g.nb + lead;
+  int c = row_ptr[r + 1] - row_ptr[r];
+  if (partner >= 0) c += row_ptr[r - lead + partner + 1] - row_ptr[r - lead + partner];
+  return c;
+}
+
+__device__ __forceinline__ unsigned sched_key(const Geo& g, const int* row_ptr, int item,
+                                              int phased, int hpp) {
+  const unsigned k = (unsigned)(2 * g.nb - group_cost(g, row_ptr, item));
+  return phased ? (unsigned)((item / g.groups_per_head) / hpp) * (unsigned)(2 * g.nb + 1) + k : k;
 }
 
 __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restrict__ row_ptr,
@@ -121,19 +134,19 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
   constexpr int NT = 512;
   __shared__ unsigned offs[16][NT];
   __shared__ unsigned stmp[NT / 64 + 1];
-  const int rows = g.rows;
+  const int items = g.groups;
   if (threadIdx.x == 0) counter[0] = 0;
   if (mode == ABS_SCHED_HEAD_MAJOR) {
-    for (int r = threadIdx.x; r < rows; r += NT) sched[r] = r;
+    for (int r = threadIdx.x; r < items; r += NT) sched[r] = r;
     return;
   }
   const int phased = mode == ABS_SCHED_HEAD_PHASED;
   const int nphase = phased ? (g.B * g.H + hpp - 1) / hpp : 1;
-  const unsigned maxkey = (unsigned)nphase * (unsigned)(g.nb + 1);
+  const unsigned maxkey = (unsigned)nphase * (unsigned)(2 * g.nb + 1);
   int passes = 1;
   while (passes < 8 && (maxkey >> (4 * passes)) != 0u) ++passes;
-  const int per = (rows + NT - 1) / NT;
-  const int lo = threadIdx.x * per, hi = min(rows, lo + per);
+  const int per = (items + NT - 1) / NT;
+  const int lo = threadIdx.x * per, hi = min(items, lo + per);
   for (int pass = 0; pass < passes; ++pass) {
     const int* src = pass == 0 ? nullptr : ((pass & 1) ? buf_a : buf_b);
     int* dst = pass == passes - 1 ? sched : ((pass & 1) ? buf_b : buf_a);
@@ -143,7 +156,7 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
     for (int x = 0; x < 16; ++x) cnt[x] = 0u;
     for (int e = lo; e < hi; ++e) {
       const int r = src ? src[e] : e;
-      const unsigned dg = (sched_key(row_ptr, r, g.nb, phased, hpp) >> sh) & 15u;
+      const unsigned dg = (sched_key(g, row_ptr, r, phased, hpp) >> sh) & 15u;
 #pragma unroll
       for (int x = 0; x < 16; ++x) cnt[x] += (dg == (unsigned)x) ? 1u : 0u;
     }
@@ -170,7 +183,7 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
     __syncthreads();
     for (int e = lo; e < hi; ++e) {
       const int r = src ? src[e] : e;
-      const unsigned dg = (sched_key(row_ptr, r, g.nb, phased, hpp) >> sh) & 15u;
+      const unsigned dg = (sched_key(g, row_ptr, r, phased, hpp) >> sh) & 15u;
       const unsigned pos = offs[dg][threadIdx.x]++;
       dst[pos] = r;
     }
@@ -181,9 +194,14 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
 __global__ void reset_counter_kernel(int* counter) { counter[0] = 0; }
 
 // ---------------------------------------------------------------------------
-// bf16 block-sparse attention, one workgroup of BT/32 waves per item (query
-// block).  Wave w owns query slots 32w .. 32w+31.  Per kept key block j, in
-// chunks of 64 keys:
+// bf16 block-sparse attention.  A workgroup handles one work item: a pair of
+// neighbouring query blocks of one head (or a single block), 4 waves per
+// query block (BT = 128), wave w owning query slots 32*(w%NW1) .. +31 of block
+// w/NW1.  The workgroup walks the union of the two ascending kept-block lists;
+// each K/V tile is copied into LDS once and serves both blocks, which halves
+// the K/V traffic per flop (neighbouring blocks keep nearly the same key
+// blocks).  Per kept key block j, for the waves whose block keeps j, in chunks
+// of 64 keys:
 //   S^T (keys x queries) = K_j Q^T with v_mfma_f32_32x32x16_bf16 (Q^T held in
 //     registers as the B operand, K_j read from LDS as the A operand);
 //   padding keys get -1e30 through one extra MFMA k-step (bias column times a
@@ -192,18 +210,18 @@ __global__ void reset_counter_kernel(int* counter) { counter[0] = 0; }
 //     with log2(e)/sqrt(d) folded into one FMA;
 //   O^T (d x queries) += Vt_j P^T, the probabilities converted to bf16 straight
 //     from the accumulator layout (see vt_perm).
-// K_j and V_j arrive through direct global->LDS loads (global_load_lds_dwordx4)
-// of the chunk-major tiles; K_{j+1} is fetched while the softmax and PV of
-// block j run, V_{j+1} while the QK^T and softmax of block j+1 run.
-// PERSIST: workgroups pull items (sched order) from an atomic queue until it is
-// exhausted; otherwise one workgroup per item.
+// K/V tiles are double buffered: the direct global->LDS copies of the next
+// union block (global_load_lds_dwordx4) run while the current one is
+// computed; one barrier per block.  PERSIST: workgroups pull work items from
+// an atomic queue (sched order) until it is exhausted.
 // ---------------------------------------------------------------------------
 template <int D, int BT>
 struct AttnCfg {
-  static constexpr int NW = BT / 32, NT = 64 * NW;
+  static constexpr int NW1 = BT / 32;               // waves per query block
+  static constexpr int NW = 2 * NW1, NT = 64 * NW;   // waves / threads per workgroup
   static constexpr int TILE = BT * D * 2;            // bytes of one K or V tile
-  static constexpr int INSTR = TILE / 1024;          // 1 KB per wave-wide DMA
-  static constexpr int ROUNDS = INSTR / NW;          // DMAs per thread per tile
+  static constexpr int INSTR = TILE / 1024;          // 1 KB per wave-wide copy
+  static constexpr int ROUNDS = INSTR / NW;          // copies per thread per tile
   static constexpr int KS = D / 16, NSUB = BT / 32, DSUB = D / 32;
   static constexpr int CHS = NSUB < 2 ? NSUB : 2;    // 32-key subtiles per softmax chunk
   static constexpr int NCH = NSUB / CHS;
@@ -242,10 +260,10 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
 }
 
 template <int D, int BT, bool PERSIST>
-__global__ __launch_bounds__(2 * BT, 2) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs a) {
   using C = AttnCfg<D, BT>;
-  __shared__ __attribute__((aligned(1024))) char sK[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char sV[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char sK[2][C::TILE];
+  __shared__ __attribute__((aligned(1024))) char sV[2][C::TILE];
   __shared__ int s_off[BT];
   __shared__ int s_crd[BT];
   __shared__ int s_item;
@@ -253,6 +271,7 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_bf16_kernel(AttnArgs a) {
   const Geo& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = w / C::NW1, wq = w % C::NW1;   // query block of the pair, wave in block
   const int hf = lane >> 5, l32 = lane & 31;
   for (int s = tid; s < BT; s += C::NT) {
     const int plane = g.bh * g.bw;
@@ -262,85 +281,77 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_bf16_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  const uint32_t sK_base = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)sK;
-  const uint32_t sV_base = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)sV;
+  const uint32_t sK_base = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)&sK[0][0];
+  const uint32_t sV_base = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)&sV[0][0];
   // per-lane LDS byte offsets of the MFMA A operands (see the re-layout)
-  const char* kread = sK + hf * (BT * 16) + l32 * 16;
-  const char* vread = sV + hf * (D * 16) + l32 * 16;
+  const int kread = hf * (BT * 16) + l32 * 16;
+  const int vread = hf * (D * 16) + l32 * 16;
   const long long t_start = (long long)wall_clock64();
   long long tiles = 0;
 
   int iter = 0;
   while (true) {
-    int r;
+    int item;
     if (PERSIST) {
       if (tid == 0) s_item = atomicAdd(a.counter, 1);
       __syncthreads();
-      const int it = __builtin_amdgcn_readfirstlane(s_item);
-      if (it >= g.rows) break;
-      r = ld_scalar(a.sched, it);
+      item = __builtin_amdgcn_readfirstlane(s_item);
+      if (item >= g.groups) break;
+      item = ld_scalar(a.sched, item);
     } else {
       if (iter > 0) break;
-      r = a.head_major ? (int)blockIdx.x : ld_scalar(a.sched, blockIdx.x);
+      item = a.head_major ? (int)blockIdx.x : ld_scalar(a.sched, blockIdx.x);
     }
     ++iter;
-    r = __builtin_amdgcn_readfirstlane(r);
+    item = __builtin_amdgcn_readfirstlane(item);
 
-    const int bhh = r / g.nb, iq = r % g.nb;
+    const int bhh = item / g.groups_per_head, gl = item % g.groups_per_head;
+    int lead, partner;
+    group_blocks(g, gl, &lead, &partner);
     const int b = bhh / g.H, h = bhh % g.H;
     const long tok_base = (long)b * g.N;
-    const int rp0 = ld_scalar(a.row_ptr, r);
-    const int nnz = ld_scalar(a.row_ptr, r + 1) - rp0;
-    const int* cols = a.col_idx + rp0;
+    const int rA = bhh * g.nb + lead;
+    const int rB = partner >= 0 ? bhh * g.nb + partner : -1;
+    const int pA = ld_scalar(a.row_ptr, rA), nA = ld_scalar(a.row_ptr, rA + 1) - pA;
+    const int pB = rB >= 0 ? ld_scalar(a.row_ptr, rB) : 0;
+    const int nB = rB >= 0 ? ld_scalar(a.row_ptr, rB + 1) - pB : 0;
+    const int* colsA = a.col_idx + pA;
+    const int* colsB = a.col_idx + pB;
+    const bool active = half == 0 || rB >= 0;     // this wave's query block exists
+    const int iq = half == 0 ? lead : partner;
     const char* kc_head = (const char*)(a.kc + (long)bhh * g.nb * (D * BT));
     const char* vc_head = (const char*)(a.vc + (long)bhh * g.nb * (D * BT));
 
-    // A tile is copied in NCH parts (key halves when NCH == 2), G copies per
-    // thread each.  K part h: chunk j, keys [h*BT/2, (h+1)*BT/2); V part h:
-    // key positions [h*BT/2, (h+1)*BT/2), i.e. a contiguous TILE/NCH bytes.
-    constexpr int G = C::ROUNDS / C::NCH;
-    auto issue_k = [&](int jblk, int part) {
-      const char* src = kc_head + (long)jblk * C::TILE;
+    auto issue = [&](int jblk, int buf) {
+      const char* ks = kc_head + (long)jblk * C::TILE;
+      const char* vs = vc_head + (long)jblk * C::TILE;
 #pragma unroll
-      for (int rr = 0; rr < G; ++rr) {
-        const int jx = rr * C::NW + w;
-        const int off = C::NCH == 1 ? jx * 1024 : jx * (BT * 16) + part * (BT * 8);
-        dma16(src + off + lane * 16, sK_base + off);
+      for (int rr = 0; rr < C::ROUNDS; ++rr) {
+        const int off = (rr * C::NW + w) * 1024;
+        dma16(ks + off + lane * 16, sK_base + buf * C::TILE + off);
       }
-    };
-    auto issue_v = [&](int jblk, int part) {
-      const char* src = vc_head + (long)jblk * C::TILE;
 #pragma unroll
-      for (int rr = 0; rr < G; ++rr) {
-        const int off = part * (C::TILE / C::NCH) + (rr * C::NW + w) * 1024;
-        dma16(src + off + lane * 16, sV_base + off);
+      for (int rr = 0; rr < C::ROUNDS; ++rr) {
+        const int off = (rr * C::NW + w) * 1024;
+        dma16(vs + off + lane * 16, sV_base + buf * C::TILE + off);
       }
     };
 
-    // Issue order (NCH == 2), one group = G copies per thread:
-    //   K0_j, V0_j, K1_j   (prologue for j = first, else during block j-1)
-    //   V1_j               (top of half 0 of block j)
-    //   K0_{j+1}           (middle of half 0, once every wave has read K0_j)
-    //   V0_{j+1}           (top of half 1, once every wave has read V0_j)
-    //   K1_{j+1}           (middle of half 1)
-    // so each wait below names exactly how many groups were issued after the
-    // awaited one.  NCH == 1: K_j before block j, V_j at its top.
-    int jn = ld_scalar(cols, 0);
-    if (C::NCH == 2) {
-      issue_k(jn, 0);
-      issue_v(jn, 0);
-      issue_k(jn, 1);
-    } else {
-      issue_k(jn, 0);
-    }
-    // query block geometry and this lane's query slot
-    const int tq = iq / (g.nbh * g.nbw), hq = (iq / g.nbw) % g.nbh, wq = iq % g.nbw;
-    const int n0q = ((tq * g.bt) * g.Hg + hq * g.bh) * g.W + wq * g.bw;
-    const int TlQ = g.T - tq * g.bt, HlQ = g.Hg - hq * g.bh, WlQ = g.W - wq * g.bw;
-    const int qs = 32 * w + l32;
+    // merged walk over the two ascending lists
+    constexpr int END = 0x7fffffff;
+    int ia = 0, ib = 0;
+    int nxa = nA > 0 ? ld_scalar(colsA, 0) : END;
+    int nxb = nB > 0 ? ld_scalar(colsB, 0) : END;
+    issue(min(nxa, nxb), 0);
+
+    // this lane's query slot
+    const int tq = iq / (g.nbh * g.nbw), hq = (iq / g.nbw) % g.nbh, wqb = iq % g.nbw;
+    const int n0q = ((tq * g.bt) * g.Hg + hq * g.bh) * g.W + wqb * g.bw;
+    const int TlQ = g.T - tq * g.bt, HlQ = g.Hg - hq * g.bh, WlQ = g.W - wqb * g.bw;
+    const int qs = 32 * wq + l32;
     const int qcrd = s_crd[qs];
-    const bool qvalid =
-        (qcrd & 255) < TlQ && ((qcrd >> 8) & 255) < HlQ && ((qcrd >> 16) & 255) < WlQ;
+    const bool qvalid = active && (qcrd & 255) < TlQ && ((qcrd >> 8) & 255) < HlQ &&
+                        ((qcrd >> 16) & 255) < WlQ;
     const long nq = n0q + s_off[qs];
 
     // Q^T as the B operand: lane holds 8 consecutive d of query slot qs
@@ -366,114 +377,100 @@ __global__ __launch_bounds__(2 * BT, 2) void attn_bf16_kernel(AttnArgs a) {
       for (int e = 0; e < 16; ++e) o[u][e] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int jj = 0; jj < nnz; ++jj) {
-      const int j = jn;
-      const bool more = jj + 1 < nnz;
-      jn = more ? ld_scalar(cols, jj + 1) : 0;
-      const int tb = j / (g.nbh * g.nbw), hb = (j / g.nbw) % g.nbh, wb = j % g.nbw;
-      const int Tl = g.T - tb * g.bt, Hl = g.Hg - hb * g.bh, Wl = g.W - wb * g.bw;
-      const bool partial = Tl < g.bt || Hl < g.bh || Wl < g.bw;
+    int buf = 0;
+    while (nxa != END || nxb != END) {
+      const int j = min(nxa, nxb);
+      const bool needA = nxa == j, needB = nxb == j;
+      if (needA) { ++ia; nxa = ia < nA ? ld_scalar(colsA, ia) : END; }
+      if (needB) { ++ib; nxb = ib < nB ? ld_scalar(colsB, ib) : END; }
+      const int jn = min(nxa, nxb);
+      const bool mine = half == 0 ? needA : needB;
 
-#pragma unroll
-      for (int hc = 0; hc < C::NCH; ++hc) {
-        // ---- top: K part hc of block j has landed; V part (hc-1) is free
-        if (C::NCH == 2) {
-          if (hc == 0) wait_vmcnt<2 * G>();
-          else if (more) wait_vmcnt<2 * G>();
-          else wait_vmcnt<G>();
-        } else {
-          wait_vmcnt<0>();
-        }
-        wg_barrier();
-        if (C::NCH == 2) {
-          if (hc == 0) issue_v(j, 1);
-          else if (more) issue_v(jn, 0);
-        } else {
-          issue_v(j, 0);
-        }
+      wait_vmcnt<0>();      // this thread's copies of block j have landed
+      wg_barrier();         // ... everyone's; and block j-1's buffer is free
+      if (jn != END) issue(jn, buf ^ 1);
 
-        // ---- S^T = K Q^T for the CHS key subtiles of this part
-        f32x16_t s[C::CHS];
+      if (mine) {
+        const int tb = j / (g.nbh * g.nbw), hb = (j / g.nbw) % g.nbh, wb = j % g.nbw;
+        const int Tl = g.T - tb * g.bt, Hl = g.Hg - hb * g.bh, Wl = g.W - wb * g.bw;
+        const bool partial = Tl < g.bt || Hl < g.bh || Wl < g.bw;
+        const char* kb = sK[buf] + kread;
+        const char* vb = sV[buf] + vread;
 #pragma unroll
-        for (int t2 = 0; t2 < C::CHS; ++t2) {
-          const int t = hc * C::CHS + t2;
+        for (int hc = 0; hc < C::NCH; ++hc) {
+          // ---- S^T = K Q^T for the CHS key subtiles of this chunk
+          f32x16_t s[C::CHS];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) s[t2][e] = 0.f;
+          for (int t2 = 0; t2 < C::CHS; ++t2) {
+            const int t = hc * C::CHS + t2;
 #pragma unroll
-          for (int ks = 0; ks < C::KS; ++ks) {
-            const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(
-                kread + ks * (2 * BT * 16) + t * 512);
-            s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qop[ks], s[t2], 0, 0, 0);
+            for (int e = 0; e < 16; ++e) s[t2][e] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) {
+              const bf16x8_t av =
+                  *reinterpret_cast<const bf16x8_t*>(kb + ks * (2 * BT * 16) + t * 512);
+              s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qop[ks], s[t2], 0, 0, 0);
+            }
+            if (partial) {
+              // padding keys: add -1e30 through one extra k-step (bias column x ones row)
+              const int crd = s_crd[32 * t + l32];
+              const bool ok =
+                  (crd & 255) < Tl && ((crd >> 8) & 255) < Hl && ((crd >> 16) & 255) < Wl;
+              bf16x8_t bias, ones;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) { bias[e] = (__bf16)0.0f; ones[e] = (__bf16)0.0f; }
+              if (hf == 0) ones[0] = (__bf16)1.0f;
+              if (hf == 0 && !ok) bias[0] = (__bf16)(-1.0e30f);
+              s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias, ones, s[t2], 0, 0, 0);
+            }
           }
-          if (partial) {
-            // padding keys: add -1e30 through one extra k-step (bias column x ones row)
-            const int crd = s_crd[32 * t + l32];
-            const bool ok =
-                (crd & 255) < Tl && ((crd >> 8) & 255) < Hl && ((crd >> 16) & 255) < Wl;
-            bf16x8_t bias, ones;
+
+          // ---- online softmax over the chunk's keys, per query column
+          float mt = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { bias[e] = (__bf16)0.0f; ones[e] = (__bf16)0.0f; }
-            if (hf == 0) ones[0] = (__bf16)1.0f;
-            if (hf == 0 && !ok) bias[0] = (__bf16)(-1.0e30f);
-            s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias, ones, s[t2], 0, 0, 0);
+          for (int t2 = 0; t2 < C::CHS; ++t2)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[t2][e]);
+          mt = fmaxf(mt, __shfl_xor(mt, 32));
+          const float m_new = fmaxf(m_run, mt);
+          const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+          const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * a.c);
+          const float mc = m_use * a.c;
+          bf16x8_t pop[2 * C::CHS];
+          float psum = 0.f;
+#pragma unroll
+          for (int t2 = 0; t2 < C::CHS; ++t2)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const float pv = __builtin_amdgcn_exp2f(fmaf(s[t2][e], a.c, -mc));
+              psum += pv;
+              pop[2 * t2 + e / 8][e % 8] = (__bf16)pv;
+            }
+          l_run = l_run * alpha + psum;
+          if (m_new != m_run) {
+#pragma unroll
+            for (int u = 0; u < C::DSUB; ++u)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) o[u][e] *= alpha;
           }
-        }
+          m_run = m_new;
 
-        // ---- middle: V part hc has landed; every wave is done with K part hc
-        if (C::NCH == 2) {
-          if (hc == 0) wait_vmcnt<2 * G>();
-          else if (more) wait_vmcnt<2 * G>();
-          else wait_vmcnt<0>();
-        } else {
-          wait_vmcnt<0>();
-        }
-        wg_barrier();
-        if (more) issue_k(jn, hc);
-
-        // ---- online softmax over the part's keys, per query column
-        float mt = -INFINITY;
+          // ---- O^T += Vt P^T over the chunk's keys
 #pragma unroll
-        for (int t2 = 0; t2 < C::CHS; ++t2)
+          for (int u = 0; u < C::DSUB; ++u) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[t2][e]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * a.c);
-        const float mc = m_use * a.c;
-        bf16x8_t pop[2 * C::CHS];
-        float psum = 0.f;
-#pragma unroll
-        for (int t2 = 0; t2 < C::CHS; ++t2)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(s[t2][e], a.c, -mc));
-            psum += pv;
-            pop[2 * t2 + e / 8][e % 8] = (__bf16)pv;
-          }
-        l_run = l_run * alpha + psum;
-        if (m_new != m_run) {
-#pragma unroll
-          for (int u = 0; u < C::DSUB; ++u)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) o[u][e] *= alpha;
-        }
-        m_run = m_new;
-
-        // ---- O^T += Vt P^T over the part's keys
-#pragma unroll
-        for (int u = 0; u < C::DSUB; ++u) {
-#pragma unroll
-          for (int st2 = 0; st2 < 2 * C::CHS; ++st2) {
-            const int st = hc * 2 * C::CHS + st2;
-            const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(
-                vread + st * (2 * D * 16) + u * 512);
-            o[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pop[st2], o[u], 0, 0, 0);
+            for (int st2 = 0; st2 < 2 * C::CHS; ++st2) {
+              const int st = hc * 2 * C::CHS + st2;
+              const bf16x8_t av =
+                  *reinterpret_cast<const bf16x8_t*>(vb + st * (2 * D * 16) + u * 512);
+              o[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pop[st2], o[u], 0, 0, 0);
+            }
           }
         }
       }
+      buf ^= 1;
     }
-    tiles += nnz;
+    tiles += nA + nB;
 
     // ---- epilogue: normalise and store the real query rows
     const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -522,7 +519,9 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(Geo g, const float* __res
   __shared__ float sv[32][D];
   __shared__ int kval[32];
   const long long t_start = (long long)wall_clock64();
-  const int r = head_major ? (int)blockIdx.x : sched[blockIdx.x];
+  const int r = (int)blockIdx.x;  // rows in natural order (small float32 workloads)
+  (void)sched;
+  (void)head_major;
   const int bhh = r / g.nb, iq = r % g.nb;
   const int b = bhh / g.H, h = bhh % g.H;
   const int plane = g.bh * g.bw;
@@ -656,7 +655,7 @@ static int persistent_grid() {
   int occ = dev < 64 ? __atomic_load_n(&cache_occ[dev][slot], __ATOMIC_RELAXED) : 0;
   if (occ == 0) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &occ, reinterpret_cast<const void*>(&attn_bf16_kernel<D, BT, true>), 2 * BT, 0) !=
+            &occ, reinterpret_cast<const void*>(&attn_bf16_kernel<D, BT, true>), 4 * BT, 0) !=
             hipSuccess ||
         occ < 1)
       occ = 1;
@@ -666,7 +665,8 @@ static int persistent_grid() {
 }
 
 int attend_grid(const Geo& g, int dtype, int sched) {
-  if (dtype != ABS_BF16 || sched == ABS_SCHED_HEAD_MAJOR) return g.rows;
+  if (dtype != ABS_BF16) return g.rows;           // float32: one workgroup per row
+  if (sched == ABS_SCHED_HEAD_MAJOR) return g.groups;
   if (g.d == 128) {
     if (g.Bt == 128) return persistent_grid<128, 128>();
     if (g.Bt == 64) return persistent_grid<128, 64>();
@@ -680,9 +680,9 @@ int attend_grid(const Geo& g, int dtype, int sched) {
 template <int D, int BT>
 static void launch_bf16(const AttnArgs& a, bool persist, int grid, hipStream_t s) {
   if (persist)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, BT, true>), dim3(grid), dim3(2 * BT), 0, s, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, BT, true>), dim3(grid), dim3(4 * BT), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, BT, false>), dim3(grid), dim3(2 * BT), 0, s, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, BT, false>), dim3(grid), dim3(4 * BT), 0, s, a);
 }
 
 hipError_t launch_attend_run(const Geo& g, int dtype, const void* q, const void* k,

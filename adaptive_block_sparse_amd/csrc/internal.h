@@ -18,7 +18,32 @@ struct Geo {
   int N;               // tokens
   int rows;            // B*H*nb
   int words;           // 32-bit words of one row bitmap, ceil(nb/32)
+  // Attention work items pair two query blocks that are neighbours along one
+  // block axis (they share most kept key blocks, so one K/V tile serves both).
+  int pair_axis;       // 0 = t, 1 = h, 2 = w, -1 = no pairing (nb == 1)
+  int pair_stride;     // block-index distance to the partner
+  int groups_per_head; // work items per head
+  int groups;          // B*H*groups_per_head
 };
+
+// Leader block and partner (or -1) of group gl of a head.
+__host__ __device__ inline void group_blocks(const Geo& g, int gl, int* lead, int* partner) {
+  int i, c, n;
+  if (g.pair_axis == 0) {
+    const int plane = g.nbh * g.nbw, tg = gl / plane;
+    i = gl + tg * plane; c = 2 * tg; n = g.nbt;
+  } else if (g.pair_axis == 1) {
+    const int hh = (g.nbh + 1) / 2, wb = gl % g.nbw, hg = (gl / g.nbw) % hh, tb = gl / (g.nbw * hh);
+    i = (tb * g.nbh + 2 * hg) * g.nbw + wb; c = 2 * hg; n = g.nbh;
+  } else if (g.pair_axis == 2) {
+    const int wh = (g.nbw + 1) / 2, wg = gl % wh, rest = gl / wh;
+    i = rest * g.nbw + 2 * wg; c = 2 * wg; n = g.nbw;
+  } else {
+    *lead = gl; *partner = -1; return;
+  }
+  *lead = i;
+  *partner = (c + 1 < n) ? i + g.pair_stride : -1;
+}
 
 // Route workspace layout (byte offsets, all 256-aligned).
 struct RouteWs {

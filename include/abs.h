@@ -55,15 +55,15 @@ typedef enum {
 typedef enum { ABS_F32 = 0, ABS_BF16 = 1 } abs_dtype;
 
 /* Order in which (batch, head, query-block) items are processed by attend.
- *   NNZ_SORTED : persistent workgroups pull items from one queue sorted by the
- *                row's kept-block count, largest first, ties by row index
+ *   NNZ_SORTED : persistent workgroups pull work items from one queue sorted
+ *                by kept-block count, largest first, ties by item index
  *                (load balancing of the explainer's "Core method" part 2,
  *                recast over compute units);
- *   HEAD_MAJOR : one workgroup per item in natural (b, h, i) order, scheduled
+ *   HEAD_MAJOR : one workgroup per work item in natural order, scheduled
  *                by the hardware dispatcher (the unbalanced baseline);
  *   HEAD_PHASED: persistent queue; heads are taken in phases of a few heads
- *                (so their K/V stay cache resident), largest rows first inside
- *                a phase, ties by row index.
+ *                (so their K/V stay cache resident), largest items first
+ *                inside a phase, ties by item index.
  * All three give bitwise identical outputs: every row has one owner and a
  * fixed key-block order. */
 typedef enum {
@@ -131,10 +131,15 @@ abs_status abs_route(const abs_plan* plan, const void* q, const void* k, float p
                      size_t ws_bytes, void* stream);
 
 /* Attention prologue: re-lays k and v block-major for the attention kernel
- * (bf16) and builds the item order of `sched` from the mask's row lengths
- * (explainer "Core method" part 2: profile the mask size per head, heaviest
- * first).  On return (stream order) the workspace starts with that order,
- * int32 [rows].
+ * (bf16) and builds the order of `sched` over the attention work items from
+ * the mask's row lengths (explainer "Core method" part 2: profile the mask
+ * size per head, heaviest first).  A bf16 work item is a pair of query blocks
+ * of one head that are neighbours along t (else h, else w): the block with an
+ * even coordinate on that axis and its successor, or that block alone at the
+ * end of an odd axis; items are numbered head by head, leaders in ascending
+ * block order, and an item's cost is the kept-block count of its rows.  On
+ * return (stream order) the workspace starts with the item order, int32
+ * [items].  Float32 plans process rows in natural order.
  *   k, v : device [B, N, H, d] of the plan's dtype
  *   ws   : device workspace of at least plan->attend_ws_bytes bytes; it must
  *          be passed unchanged to abs_attend_run.                          */

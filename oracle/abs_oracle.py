@@ -356,27 +356,28 @@ def dense_attention(Q, K, V) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Work schedule
 # --------------------------------------------------------------------------
-def schedule(row_ptr, mode: str, rows_per_head: Optional[int] = None,
+def schedule(costs, mode: str, items_per_head: Optional[int] = None,
              heads_per_phase: int = 1) -> np.ndarray:
-    """Order in which the (batch, head, query-block) items are processed.
+    """Order in which work items are processed.
 
     Source: FVAttn explainer, part 2 (runtime load balancing: measure each
     head's mask size before the kernel runs and hand the heaviest work out
-    first).  Reading on one GPU: items are rows of the block mask, their cost is
-    the row's kept-block count, and the compute units pull items from one queue.
-      "head_major": rows in their natural (b, h, i) order;
-      "nnz_sorted": kept-block count descending, ties by row index;
+    first).  Reading on one GPU: an item is a row of the block mask (or a
+    group of rows of one head processed together), its cost is its kept-block
+    count, and the compute units pull items from one queue.
+      "head_major": items in their natural order;
+      "nnz_sorted": cost descending, ties by item index;
       "head_phased": heads grouped into consecutive phases of heads_per_phase
-         heads; phases in order, inside a phase count descending, ties by row.
+         heads; phases in order, inside a phase cost descending, ties by item.
     """
-    counts = np.diff(np.asarray(row_ptr, dtype=np.int64))
-    rows = counts.shape[0]
+    costs = np.asarray(costs, dtype=np.int64)
+    n = costs.shape[0]
     if mode == "head_major":
-        return np.arange(rows, dtype=np.int64)
+        return np.arange(n, dtype=np.int64)
     if mode == "nnz_sorted":
-        return np.argsort(-counts, kind="stable").astype(np.int64)
+        return np.argsort(-costs, kind="stable").astype(np.int64)
     if mode == "head_phased":
-        phase = (np.arange(rows) // rows_per_head) // heads_per_phase
-        return np.array(sorted(range(rows), key=lambda r: (phase[r], -counts[r], r)),
+        phase = (np.arange(n) // items_per_head) // heads_per_phase
+        return np.array(sorted(range(n), key=lambda r: (phase[r], -costs[r], r)),
                         dtype=np.int64)
     raise ValueError(mode)

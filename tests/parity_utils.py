@@ -123,3 +123,30 @@ def compare_outputs(o_gpu: np.ndarray, o_ref: np.ndarray, geo, rows, H: int, dty
         assert e.max() <= TOL_BF16_MAX, e.max()
         assert e.mean() <= TOL_BF16_MEAN, e.mean()
     return float(e.max()), float(e.mean())
+
+
+def pair_groups(geo, heads: int):
+    """Work items of the bf16 attention kernel: query blocks paired with their
+    neighbour along t (else h, else w); a block with an even coordinate on that
+    axis leads, its successor (if any) is the partner.  Items are listed head
+    by head, leaders in ascending block order.  Returns [(row_a, row_b or -1)]."""
+    nbt, nbh, nbw = geo.nblk
+    if nbt >= 2:
+        axis, stride, n = 0, nbh * nbw, nbt
+    elif nbh >= 2:
+        axis, stride, n = 1, nbw, nbh
+    elif nbw >= 2:
+        axis, stride, n = 2, 1, nbw
+    else:
+        axis = None
+    out = []
+    for bh in range(heads):
+        for i in range(geo.nb):
+            if axis is None:
+                out.append((bh * geo.nb + i, -1))
+                continue
+            coord = (i // (nbh * nbw), (i // nbw) % nbh, i % nbw)[axis]
+            if coord % 2 == 0:
+                partner = bh * geo.nb + i + stride if coord + 1 < n else -1
+                out.append((bh * geo.nb + i, partner))
+    return out

@@ -18,7 +18,7 @@ import torch
 import adaptive_block_sparse_amd as A
 import oracle as O
 import synth_inputs as si
-from parity_utils import check_slack, compare_masks, compare_outputs, sample_rows
+from parity_utils import check_slack, compare_masks, compare_outputs, pair_groups, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -176,12 +176,17 @@ def test_pooled_means_and_schedule_array():
     np.testing.assert_allclose(pooled[n:].reshape(1, wl.heads, geo.nb, -1), O.pool(_np(k), geo),
                                rtol=1e-5, atol=1e-5)
     rp, _ = mask.to_host()
+    counts = np.diff(rp)
+    groups = pair_groups(geo, wl.batch * wl.heads)
+    assert sorted([r for gr in groups for r in gr if r >= 0]) == list(range(counts.size))
+    costs = [counts[a] + (counts[b] if b >= 0 else 0) for a, b in groups]
     aws = A.workspace(plan.attend_ws_bytes, DEV)
     for mode, sched in (("nnz_sorted", 0), ("head_major", 1), ("head_phased", 2)):
         A.attend_prepare(plan, k.to(DEV), v.to(DEV), mask, sched, aws)
         torch.cuda.synchronize()
-        got = aws[: int(plan.rows) * 4].view(torch.int32).cpu().numpy()
-        want = O.schedule(rp, mode, rows_per_head=geo.nb, heads_per_phase=plan.heads_per_phase)
+        got = aws[: len(groups) * 4].view(torch.int32).cpu().numpy()
+        want = O.schedule(costs, mode, items_per_head=len(groups) // wl.heads,
+                          heads_per_phase=plan.heads_per_phase)
         np.testing.assert_array_equal(got, want)
 
 

@@ -44,7 +44,9 @@ def test_plan_matches_geometry(cfg):
     assert plan.col_capacity == plan.rows * geo.nb
     assert plan.tokens == wl.tokens
     assert plan.route_ws_bytes > 0 and plan.attend_ws_bytes > 0
-    assert A.attend_grid(plan, A.SCHED_HEAD_MAJOR) == plan.rows
+    from parity_utils import pair_groups
+    items = plan.rows if wl.dtype == "f32" else len(pair_groups(geo, wl.batch * wl.heads))
+    assert A.attend_grid(plan, A.SCHED_HEAD_MAJOR) == items
 
 
 def _status_of_plan(**kw):

@@ -76,13 +76,12 @@ def _check_schedule(order, counts, key):
 def test_schedule_modes():
     rng = np.random.default_rng(0)
     counts = rng.integers(1, 9, 60)
-    row_ptr = np.concatenate([[0], np.cumsum(counts)])
-    np.testing.assert_array_equal(O.schedule(row_ptr, "head_major"), np.arange(60))
-    o = O.schedule(row_ptr, "nnz_sorted")
+    np.testing.assert_array_equal(O.schedule(counts, "head_major"), np.arange(60))
+    o = O.schedule(counts, "nnz_sorted")
     _check_schedule(o, counts, lambda r: (-counts[r], r))
-    o = O.schedule(row_ptr, "head_phased", rows_per_head=10, heads_per_phase=2)
+    o = O.schedule(counts, "head_phased", items_per_head=10, heads_per_phase=2)
     _check_schedule(o, counts, lambda r: (r // 20, -counts[r], r))
     # an explicit tiny case
-    rp = np.concatenate([[0], np.cumsum([2, 5, 5, 1, 5, 2])])
-    assert O.schedule(rp, "nnz_sorted").tolist() == [1, 2, 4, 0, 5, 3]
-    assert O.schedule(rp, "head_phased", rows_per_head=3).tolist() == [1, 2, 0, 4, 5, 3]
+    c = [2, 5, 5, 1, 5, 2]
+    assert O.schedule(c, "nnz_sorted").tolist() == [1, 2, 4, 0, 5, 3]
+    assert O.schedule(c, "head_phased", items_per_head=3).tolist() == [1, 2, 0, 4, 5, 3]
