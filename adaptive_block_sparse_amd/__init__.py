@@ -24,9 +24,9 @@ LIB_PATH = os.environ.get("ABS_LIBRARY") or os.path.join(HERE, "libabs.so")
 
 OK, EINVAL, ENOTSUP, ENOSPACE, EHIP = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
-SCHED_NNZ_SORTED, SCHED_HEAD_MAJOR, SCHED_HEAD_PHASED = 0, 1, 2
+SCHED_NNZ_SORTED, SCHED_HEAD_MAJOR, SCHED_HEAD_PHASED, SCHED_XCD_LOCAL = 0, 1, 2, 3
 SCHEDULES = {"nnz_sorted": SCHED_NNZ_SORTED, "head_major": SCHED_HEAD_MAJOR,
-             "head_phased": SCHED_HEAD_PHASED}
+             "head_phased": SCHED_HEAD_PHASED, "xcd_local": SCHED_XCD_LOCAL}
 EXPORTS = ("abs_plan_init", "abs_route", "abs_attend_prepare", "abs_attend_run",
            "abs_attend", "abs_attend_grid", "abs_status_string")
 

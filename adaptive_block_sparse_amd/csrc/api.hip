@@ -70,7 +70,7 @@ AttendWs attend_ws_layout(const Geo& g, int dtype) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
   L.sched = take((size_t)g.rows * sizeof(int));
-  L.counter = take(64 * sizeof(int));
+  L.counter = take(512 * sizeof(int));
   L.sort_a = take((size_t)g.rows * sizeof(int));
   L.sort_b = take((size_t)g.rows * sizeof(int));
   if (dtype == ABS_BF16) {
@@ -176,7 +176,7 @@ abs_status abs_attend_prepare(const abs_plan* plan, const void* k, const void* v
                               const abs_mask* mask, int32_t sched, void* ws, size_t ws_bytes,
                               void* stream) {
   if (!plan_ok(plan) || !k || !v || !mask_ok(mask) || !ws) return ABS_EINVAL;
-  if (sched < ABS_SCHED_NNZ_SORTED || sched > ABS_SCHED_HEAD_PHASED) return ABS_EINVAL;
+  if (sched < ABS_SCHED_NNZ_SORTED || sched > ABS_SCHED_XCD_LOCAL) return ABS_EINVAL;
   Geo g = make_geo(plan);
   AttendWs L = attend_ws_layout(g, plan->s.dtype);
   if (ws_bytes < L.total) return ABS_ENOSPACE;
@@ -187,7 +187,7 @@ abs_status abs_attend_prepare(const abs_plan* plan, const void* k, const void* v
 
 abs_status abs_attend_grid(const abs_plan* plan, int32_t sched, int32_t* workgroups) {
   if (!plan_ok(plan) || !workgroups) return ABS_EINVAL;
-  if (sched < ABS_SCHED_NNZ_SORTED || sched > ABS_SCHED_HEAD_PHASED) return ABS_EINVAL;
+  if (sched < ABS_SCHED_NNZ_SORTED || sched > ABS_SCHED_XCD_LOCAL) return ABS_EINVAL;
   Geo g = make_geo(plan);
   const int n = attend_grid(g, plan->s.dtype, sched);
   if (n <= 0) return ABS_EHIP;
@@ -199,7 +199,7 @@ abs_status abs_attend_run(const abs_plan* plan, const void* q, const void* k,
                           const abs_mask* mask, void* o, int32_t sched, void* ws,
                           size_t ws_bytes, int64_t* telemetry, void* stream) {
   if (!plan_ok(plan) || !q || !k || !o || !mask_ok(mask) || !ws) return ABS_EINVAL;
-  if (sched < ABS_SCHED_NNZ_SORTED || sched > ABS_SCHED_HEAD_PHASED) return ABS_EINVAL;
+  if (sched < ABS_SCHED_NNZ_SORTED || sched > ABS_SCHED_XCD_LOCAL) return ABS_EINVAL;
   Geo g = make_geo(plan);
   AttendWs L = attend_ws_layout(g, plan->s.dtype);
   if (ws_bytes < L.total) return ABS_ENOSPACE;

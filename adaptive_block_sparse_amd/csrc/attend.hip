@@ -9,6 +9,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -136,8 +138,71 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
   __shared__ unsigned stmp[NT / 64 + 1];
   const int items = g.groups;
   if (threadIdx.x == 0) counter[0] = 0;
+  if (threadIdx.x < NXCD) counter[QHEAD + 32 * threadIdx.x] = 0;
   if (mode == ABS_SCHED_HEAD_MAJOR) {
     for (int r = threadIdx.x; r < items; r += NT) sched[r] = r;
+    return;
+  }
+  if (mode == ABS_SCHED_XCD_LOCAL) {
+    // head costs, then LPT placement of heads on XCDs (longest first onto the
+    // least loaded XCD, ties to the lower index); beyond MAX_LPT_HEADS heads,
+    // head h goes to XCD h % NXCD
+    __shared__ int hcost[MAX_LPT_HEADS];
+    __shared__ int hbase[MAX_LPT_HEADS];
+    __shared__ int qlen[NXCD];
+    const int heads = g.B * g.H;
+    const bool lpt = heads <= MAX_LPT_HEADS;
+    if (lpt) {
+      for (int hh = threadIdx.x; hh < heads; hh += NT) {
+        int c = 0;
+        for (int gl = 0; gl < g.groups_per_head; ++gl)
+          c += group_cost(g, row_ptr, hh * g.groups_per_head + gl);
+        hcost[hh] = c;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      long long load[NXCD];
+      int rank[NXCD];
+      for (int x = 0; x < NXCD; ++x) { load[x] = 0; rank[x] = 0; }
+      for (int n = 0; n < heads && lpt; ++n) {
+        // next head in (cost desc, index asc) order; placed heads hold a
+        // negative cost
+        int best = -1;
+        for (int hh = 0; hh < heads; ++hh) {
+          if (hcost[hh] < 0) continue;
+          if (best < 0 || hcost[hh] > hcost[best]) best = hh;
+        }
+        int xm = 0;
+        for (int x = 1; x < NXCD; ++x)
+          if (load[x] < load[xm]) xm = x;
+        load[xm] += hcost[best];
+        hbase[best] = xm * MAX_LPT_HEADS + rank[xm]++;   // (xcd, rank) packed
+        hcost[best] = -1 - hcost[best];                   // placed
+      }
+      for (int x = 0; x < NXCD; ++x) qlen[x] = 0;
+      if (lpt) {
+        for (int x = 0; x < NXCD; ++x) qlen[x] = rank[x] * g.groups_per_head;
+      } else {
+        for (int hh = 0; hh < heads; ++hh) qlen[hh % NXCD] += g.groups_per_head;
+      }
+      int off = 0;
+      for (int x = 0; x < NXCD; ++x) { counter[QOFF + x] = off; off += qlen[x]; }
+      counter[QOFF + NXCD] = off;
+      for (int x = 0; x < NXCD; ++x) qlen[x] = counter[QOFF + x];   // now queue starts
+    }
+    __syncthreads();
+    for (int it = threadIdx.x; it < items; it += NT) {
+      const int hh = it / g.groups_per_head, gl = it % g.groups_per_head;
+      int pos;
+      if (lpt) {
+        const int x = hbase[hh] / MAX_LPT_HEADS, rk = hbase[hh] % MAX_LPT_HEADS;
+        pos = qlen[x] + rk * g.groups_per_head + gl;
+      } else {
+        pos = qlen[hh % NXCD] + (hh / NXCD) * g.groups_per_head + gl;
+      }
+      sched[pos] = it;
+    }
     return;
   }
   const int phased = mode == ABS_SCHED_HEAD_PHASED;
@@ -191,7 +256,10 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
   }
 }
 
-__global__ void reset_counter_kernel(int* counter) { counter[0] = 0; }
+__global__ void reset_counter_kernel(int* counter) {
+  if (threadIdx.x == 0) counter[0] = 0;
+  if (threadIdx.x < NXCD) counter[QHEAD + 32 * threadIdx.x] = 0;
+}
 
 // ---------------------------------------------------------------------------
 // bf16 block-sparse attention.  A workgroup handles one work item: a pair of
@@ -241,6 +309,7 @@ struct AttnArgs {
   long long* telem;
   float c;  // log2(e) / sqrt(d)
   int head_major;
+  int xcd_local;
 };
 
 typedef __attribute__((address_space(4))) const int cint_t;  // scalar-loadable
@@ -293,7 +362,23 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
   while (true) {
     int item;
     if (PERSIST) {
-      if (tid == 0) s_item = atomicAdd(a.counter, 1);
+      if (tid == 0) {
+        if (a.xcd_local) {
+          // own XCD's queue first, then steal from the others in turn
+          const int x0 = (int)(xcc_id_reg() & (NXCD - 1));
+          int found = g.groups;
+          for (int k = 0; k < NXCD; ++k) {
+            const int x = (x0 + k) & (NXCD - 1);
+            const int q0 = a.counter[QOFF + x], q1 = a.counter[QOFF + x + 1];
+            if (q0 == q1) continue;
+            const int idx = atomicAdd(&a.counter[QHEAD + 32 * x], 1);
+            if (q0 + idx < q1) { found = q0 + idx; break; }
+          }
+          s_item = found;
+        } else {
+          s_item = atomicAdd(a.counter, 1);
+        }
+      }
       __syncthreads();
       item = __builtin_amdgcn_readfirstlane(s_item);
       if (item >= g.groups) break;
@@ -353,6 +438,7 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
     const bool qvalid = active && (qcrd & 255) < TlQ && ((qcrd >> 8) & 255) < HlQ &&
                         ((qcrd >> 16) & 255) < WlQ;
     const long nq = n0q + s_off[qs];
+    const bool wave_has_q = __any(qvalid);   // some real query in this wave's 32 slots
 
     // Q^T as the B operand: lane holds 8 consecutive d of query slot qs
     bf16x8_t qop[C::KS];
@@ -390,7 +476,7 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
       wg_barrier();         // ... everyone's; and block j-1's buffer is free
       if (jn != END) issue(jn, buf ^ 1);
 
-      if (mine) {
+      if (mine && wave_has_q) {
         const int tb = j / (g.nbh * g.nbw), hb = (j / g.nbw) % g.nbh, wb = j % g.nbw;
         const int Tl = g.T - tb * g.bt, Hl = g.Hg - hb * g.bh, Wl = g.W - wb * g.bw;
         const bool partial = Tl < g.bt || Hl < g.bh || Wl < g.bw;
@@ -398,6 +484,9 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
         const char* vb = sV[buf] + vread;
 #pragma unroll
         for (int hc = 0; hc < C::NCH; ++hc) {
+          // a chunk whose first slot already lies beyond the block's last real
+          // frame holds only padding keys: nothing to add
+          if ((hc * C::CHS * 32) / (g.bh * g.bw) >= Tl) continue;
           // ---- S^T = K Q^T for the CHS key subtiles of this chunk
           f32x16_t s[C::CHS];
 #pragma unroll
@@ -705,7 +794,8 @@ hipError_t launch_attend_run(const Geo& g, int dtype, const void* q, const void*
     a.c = (float)(1.4426950408889634 / sqrt((double)g.d));
     a.head_major = head_major ? 1 : 0;
     const bool persist = !head_major;
-    if (persist) hipLaunchKernelGGL(reset_counter_kernel, dim3(1), dim3(1), 0, s, a.counter);
+    a.xcd_local = sched == ABS_SCHED_XCD_LOCAL ? 1 : 0;
+    if (persist) hipLaunchKernelGGL(reset_counter_kernel, dim3(1), dim3(64), 0, s, a.counter);
     if (g.d == 128) {
       if (g.Bt == 128) launch_bf16<128, 128>(a, persist, grid, s);
       else if (g.Bt == 64) launch_bf16<128, 64>(a, persist, grid, s);

@@ -60,7 +60,8 @@ struct RouteWs {
 // Attend workspace layout.
 struct AttendWs {
   size_t sched;           // int32 [rows]
-  size_t counter;         // int32 [64] queue head (+ padding)
+  size_t counter;         // int32 [512]: [0] queue head; [32..40] XCD queue offsets;
+                          // [64 + 32x] head of XCD queue x (own cache line each)
   size_t sort_a, sort_b;  // int32 [rows] each, radix-sort ping-pong
   size_t kc, vc;          // bf16: chunk-major K and V block tiles [B*H*nb*Bt*d] each;
                           // float32: vc holds a token-major copy of V, kc is empty
@@ -85,5 +86,10 @@ hipError_t launch_attend_run(const Geo& g, int dtype, const void* q, const void*
 int attend_grid(const Geo& g, int dtype, int sched);
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+constexpr int NXCD = 8;          // XCDs (L2 domains) of an MI355X
+constexpr int QOFF = 32;         // counter[QOFF + x]: start of XCD queue x (x = 0..NXCD)
+constexpr int QHEAD = 64;        // counter[QHEAD + 32 x]: pull counter of XCD queue x
+constexpr int MAX_LPT_HEADS = 1024;
 
 }  // namespace abs_impl

@@ -94,7 +94,7 @@ def main():
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--p", type=float, default=None)
     ap.add_argument("--sched", default="head_phased",
-                    choices=["nnz_sorted", "head_major", "head_phased"])
+                    choices=["nnz_sorted", "head_major", "head_phased", "xcd_local"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for HBM counter scaling)")
@@ -180,16 +180,30 @@ def main():
     rows_i = np.repeat(np.arange(rp.size - 1) % nb, np.diff(rp))
     valid_flops = 4.0 * d * float((nvalid[rows_i] * nvalid[ci]).sum())
 
-    # per-CU balance: the timed schedule and the naive head-major launch
+    # per-CU balance and kernel time under every schedule (the naive
+    # head-major hardware dispatch included)
     bal = {}
-    for name, s in (("timed", sched), ("nnz_sorted", A.SCHED_NNZ_SORTED),
-                    ("head_major", A.SCHED_HEAD_MAJOR)):
-        tel = torch.zeros(A.attend_grid(plan, s) * 4, dtype=torch.int64, device=dev)
-        A.attend(plan, q, k, v, mask, sched=s, o=torch.empty_like(q), ws=aws, telemetry=tel)
+    o2 = torch.empty_like(q)
+    for name, s in A.SCHEDULES.items():
+        try:
+            n_wg = A.attend_grid(plan, s)
+        except A.AbsError:
+            continue
+        tel = torch.zeros(n_wg * 4, dtype=torch.int64, device=dev)
+        A.attend_prepare(plan, k, v, mask, s, aws)
+        A.attend_run(plan, q, k, mask, o2, s, aws, telemetry=tel)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(3):
+            A.attend_run(plan, q, k, mask, o2, s, aws)
+        e1.record(stream)
         torch.cuda.synchronize()
         t = tel.cpu().numpy().reshape(-1, 4)
         assert int(t[:, 2].sum()) == nnz
         bal[name] = imbalance(t)
+        bal[name]["ms_attend_kernel"] = round(e0.elapsed_time(e1) / 3, 4)
+        bal[name]["xcds_seen"] = int(len(set((t[:, 1] & 0xF).tolist())))
+    A.attend_prepare(plan, k, v, mask, sched, aws)   # restore the timed schedule
 
     dense_ms = None
     cpu = None

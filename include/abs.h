@@ -64,12 +64,20 @@ typedef enum { ABS_F32 = 0, ABS_BF16 = 1 } abs_dtype;
  *   HEAD_PHASED: persistent queue; heads are taken in phases of a few heads
  *                (so their K/V stay cache resident), largest items first
  *                inside a phase, ties by item index.
- * All three give bitwise identical outputs: every row has one owner and a
+ *   XCD_LOCAL  : heads are placed on the GPU's 8 XCDs (longest head first onto
+ *                the least loaded XCD); each XCD has its own queue of its
+ *                heads' work items in natural (spatial) order, so neighbouring
+ *                items that share key blocks run together under one L2; a
+ *                workgroup pops from the queue of the XCD it runs on (read from
+ *                the hardware XCC id) and steals from the others once that
+ *                queue is empty.
+ * All of them give bitwise identical outputs: every row has one owner and a
  * fixed key-block order. */
 typedef enum {
   ABS_SCHED_NNZ_SORTED = 0,
   ABS_SCHED_HEAD_MAJOR = 1,
-  ABS_SCHED_HEAD_PHASED = 2
+  ABS_SCHED_HEAD_PHASED = 2,
+  ABS_SCHED_XCD_LOCAL = 3
 } abs_sched;
 
 typedef struct {

@@ -157,8 +157,9 @@ def test_slack_fill_active_long_horizon():
 def test_schedules_are_bitwise_identical():
     wl = SMALL["bf16-d128-bt128-ragged"]
     inputs = si.make_inputs(wl)
-    outs = [_run(wl, 0.8, 2, sched=s, inputs=inputs)["o"] for s in (0, 1, 2)]
-    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    outs = [_run(wl, 0.8, 2, sched=s, inputs=inputs)["o"] for s in (0, 1, 2, 3)]
+    for other in outs[1:]:
+        assert np.array_equal(outs[0], other)
 
 
 def test_pooled_means_and_schedule_array():
@@ -181,13 +182,26 @@ def test_pooled_means_and_schedule_array():
     assert sorted([r for gr in groups for r in gr if r >= 0]) == list(range(counts.size))
     costs = [counts[a] + (counts[b] if b >= 0 else 0) for a, b in groups]
     aws = A.workspace(plan.attend_ws_bytes, DEV)
+    gph = len(groups) // wl.heads
     for mode, sched in (("nnz_sorted", 0), ("head_major", 1), ("head_phased", 2)):
         A.attend_prepare(plan, k.to(DEV), v.to(DEV), mask, sched, aws)
         torch.cuda.synchronize()
         got = aws[: len(groups) * 4].view(torch.int32).cpu().numpy()
-        want = O.schedule(costs, mode, items_per_head=len(groups) // wl.heads,
-                          heads_per_phase=plan.heads_per_phase)
+        want = O.schedule(costs, mode, items_per_head=gph, heads_per_phase=plan.heads_per_phase)
         np.testing.assert_array_equal(got, want)
+    # XCD-local queues: heads placed longest first onto the least loaded of 8
+    # XCDs; queue x lists its heads' items in placement then natural order
+    A.attend_prepare(plan, k.to(DEV), v.to(DEV), mask, A.SCHED_XCD_LOCAL, aws)
+    torch.cuda.synchronize()
+    got = aws[: len(groups) * 4].view(torch.int32).cpu().numpy()
+    hcost = [sum(costs[h * gph:(h + 1) * gph]) for h in range(wl.heads)]
+    load, placed = [0] * 8, [[] for _ in range(8)]
+    for h in sorted(range(wl.heads), key=lambda h: (-hcost[h], h)):
+        x = min(range(8), key=lambda x: (load[x], x))
+        load[x] += hcost[h]
+        placed[x].append(h)
+    want = [h * gph + gl for x in range(8) for h in placed[x] for gl in range(gph)]
+    np.testing.assert_array_equal(got, want)
 
 
 def test_nan_input_keeps_mask_well_formed():
