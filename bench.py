@@ -45,6 +45,26 @@ def imbalance(tel: np.ndarray):
                 busy_max_over_mean=float(b.max() / b.mean()))
 
 
+def measured_traffic(workload_cfg: int, sched: str):
+    """HBM bytes per launch of the attention kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary, if it was taken on this workload and launch
+    and the kernel source has not changed since (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_bf16_wan22_480p_hbm_traffic.md")
+    src = os.path.join(ROOT, "adaptive_block_sparse_amd", "csrc", "attend.hip")
+    if workload_cfg != 1 or sched != "head_major" or not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "|", "#")):
+            key, _, val = line.partition(":")
+            fields[key.strip()] = val.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("attend_hip_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def block_valid_counts(grid, block) -> np.ndarray:
     """Real tokens in each 3D block (row-major block order)."""
     per_axis = []
@@ -93,7 +113,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--p", type=float, default=None)
-    ap.add_argument("--sched", default="head_phased",
+    ap.add_argument("--sched", default="head_major",
                     choices=["nnz_sorted", "head_major", "head_phased", "xcd_local"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -240,8 +260,9 @@ def main():
         "tflops_attend_kernel": round(eff_attn, 2),
         "tflops_valid_pairs_layer": round(valid_flops / (ms_step * 1e-3) / 1e12, 2),
         "roofline": {"bound": "mfma", "achieved": round(eff_attn, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(eff_attn / peak, 4), "traffic": None,
-                     "kernel": "attn_bf16_kernel<128,128,persistent>",
+                     "unit": "TFLOP/s", "frac": round(eff_attn / peak, 4),
+                     "traffic": measured_traffic(args.workload, args.sched),
+                     "kernel": "attn_bf16_kernel<128,128>",
                      "per_unit": "4*Bt^2*d flop per kept tile"},
         "route_hbm": {"bytes_read_qk": 2 * wl.tokens * wl.heads * wl.head_dim * 2,
                       "gbs_algorithmic": round(2 * wl.tokens * wl.heads * wl.head_dim * 2
