@@ -225,7 +225,34 @@ def main():
         bal[name]["xcds_seen"] = int(len(set((t[:, 1] & 0xF).tolist())))
     A.attend_prepare(plan, k, v, mask, sched, aws)   # restore the timed schedule
 
-    dense_ms = None
+    # cold step: L2 and Infinity Cache flushed by writing 512 MB first
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(3):
+        flush.fill_(1)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        step(ev)
+        torch.cuda.synchronize()
+        cold.append(ev[0].elapsed_time(ev[3]))
+    del flush
+
+    # dense comparator: the same layer with every block kept (p = 1), our own
+    # kernel; context for the explainer's sparse-over-dense attention speedup
+    dmask = A.Mask(plan, dev)
+    A.route(plan, q, k, 1.0, 1, 0.0, mask=dmask, ws=rws)
+    A.attend_prepare(plan, k, v, dmask, sched, aws)
+    A.attend_run(plan, q, k, dmask, o2, sched, aws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(2):
+        A.attend_run(plan, q, k, dmask, o2, sched, aws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dense_ms = e0.elapsed_time(e1) / 2
+    dense_tiles = int(dmask.row_ptr[-1].item())
+    del dmask
+    A.attend_prepare(plan, k, v, mask, sched, aws)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -268,6 +295,10 @@ def main():
                       "gbs_algorithmic": round(2 * wl.tokens * wl.heads * wl.head_dim * 2
                                                / (t_route * 1e-3) / 1e9, 1)},
         "imbalance": bal,
+        "ms_per_step_cold": round(float(np.median(cold)), 4),
+        "dense_p1": {"ms_attend_kernel": round(dense_ms, 4), "tiles": dense_tiles,
+                     "tflops": round(4.0 * bt * bt * d * dense_tiles / (dense_ms * 1e-3) / 1e12, 2),
+                     "speedup_sparse_over_dense": round(dense_ms / t_attn, 3)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

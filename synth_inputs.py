@@ -21,7 +21,8 @@ not available, so these stand in for them):
 * tau_h = 1 (tiny), U(1, 3) (480p, 720p, long horizon) or log-uniform over
   [0.3, 6] (head-imbalance stress);
 * seeds: numpy default_rng([cfg, head, stream]) with stream 0 = Omega, b, W;
-  1 = eps_q; 2 = eps_k; 3 = V; 4 = pair sample; temperatures use
+  1 = eps_q; 2 = eps_k; 3 = V; 4 = pair sample; batch entry b > 0 uses
+  default_rng([cfg, head, 1000 + b, stream]); temperatures use
   default_rng([cfg, 65535]);
 * tensors are laid out [B, N, H, d] and cast to the workload dtype with
   round-to-nearest-even (bf16 through torch).
@@ -90,18 +91,24 @@ def _coords(grid) -> np.ndarray:
 
 
 def head_tensors(cfg: int, head: int, grid, d: int, tau: float,
-                 n_pairs: int = 65536):
-    """Float32 Q, K, V of one head, each [N, d] (before the dtype cast)."""
+                 n_pairs: int = 65536, batch: int = 0):
+    """Float32 Q, K, V of one head, each [N, d] (before the dtype cast).
+    Batch entry b > 0 draws from seeds extended by b."""
     u = _coords(grid)
     N = u.shape[0]
-    r0 = np.random.default_rng([cfg, head, 0])
+    key = [cfg, head] if batch == 0 else [cfg, head, 1000 + batch]
+
+    def rng(stream):
+        return np.random.default_rng(key + [stream])
+
+    r0 = rng(0)
     omega = r0.normal(0.0, 0.5, (N_FEATURES, 3))
     phase = r0.uniform(0.0, 2.0 * math.pi, N_FEATURES)
     proj = r0.normal(0.0, 1.0 / math.sqrt(N_FEATURES), (N_FEATURES, d))
     phi = math.sqrt(2.0) * np.cos(2.0 * math.pi * (u @ omega.T) + phase)
     base = (phi @ proj).astype(np.float32)
-    eq = np.random.default_rng([cfg, head, 1]).standard_normal((N, d), dtype=np.float32)
-    ek = np.random.default_rng([cfg, head, 2]).standard_normal((N, d), dtype=np.float32)
+    eq = rng(1).standard_normal((N, d), dtype=np.float32)
+    ek = rng(2).standard_normal((N, d), dtype=np.float32)
     q = base + np.float32(0.3) * eq
     del eq
     k = base + np.float32(0.3) * ek
@@ -110,14 +117,14 @@ def head_tensors(cfg: int, head: int, grid, d: int, tau: float,
         lg = (q.astype(np.float64) @ k.astype(np.float64).T) / math.sqrt(d)
         sigma = float(lg.std())
     else:
-        idx = np.random.default_rng([cfg, head, 4]).integers(0, N, (n_pairs, 2))
+        idx = rng(4).integers(0, N, (n_pairs, 2))
         lg = np.einsum("ij,ij->i", q[idx[:, 0]].astype(np.float64),
                        k[idx[:, 1]].astype(np.float64)) / math.sqrt(d)
         sigma = float(lg.std())
     s = math.sqrt(2.0 / sigma)
     q *= np.float32(s / tau)
     k *= np.float32(s)
-    v = np.random.default_rng([cfg, head, 3]).standard_normal((N, d), dtype=np.float32)
+    v = rng(3).standard_normal((N, d), dtype=np.float32)
     return q, k, v
 
 
@@ -125,8 +132,8 @@ def make_inputs(wl: Workload, heads: Optional[Sequence[int]] = None, device: str
     """Q, K, V as torch tensors [B, N, H, d] in the workload dtype.
 
     ``heads`` restricts generation to a subset of head indices (the layout still
-    has len(heads) heads, in the given order); the default is all heads.  The
-    batch dimension repeats the same draw (every workload here has B = 1).
+    has len(heads) heads, in the given order); the default is all heads.  Each
+    batch entry is its own draw (batch entry 0 uses the base seeds).
     """
     import torch
 
@@ -135,11 +142,12 @@ def make_inputs(wl: Workload, heads: Optional[Sequence[int]] = None, device: str
     tdt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
     N, d = wl.tokens, wl.head_dim
     out = [torch.empty((wl.batch, N, len(hs), d), dtype=tdt) for _ in range(3)]
-    for slot, h in enumerate(hs):
-        qkv = head_tensors(wl.cfg, h, wl.grid, d, float(taus[h]))
-        for dst, src in zip(out, qkv):
-            # round-to-nearest-even cast, done by torch
-            dst[:, :, slot, :] = torch.from_numpy(src).to(tdt).unsqueeze(0)
+    for b in range(wl.batch):
+        for slot, h in enumerate(hs):
+            qkv = head_tensors(wl.cfg, h, wl.grid, d, float(taus[h]), batch=b)
+            for dst, src in zip(out, qkv):
+                # round-to-nearest-even cast, done by torch
+                dst[b, :, slot, :] = torch.from_numpy(src).to(tdt)
     if device != "cpu":
         out = [t.to(device) for t in out]
     return tuple(out)

@@ -39,6 +39,13 @@ SMALL = {
     "bf16-d64-bt128-onetile": _wl(104, (2, 8, 8), (2, 8, 8), 2, 64, "bf16"),
     "f32-d128-bt32": _wl(105, (3, 10, 9), (2, 4, 4), 2, 128, "f32"),
     "f32-tiny-cfg0": si.WORKLOADS[0],
+    "bf16-batch2": si.Workload(107, "test-107-batch2", 2, 3, 128, "bf16", (4, 10, 12), (2, 8, 8),
+                               (0.9,), 2, 0.0, "u13"),
+    "bf16-pair-h": _wl(108, (2, 16, 24), (2, 8, 8), 2, 128, "bf16"),       # nbt = 1: pairs along h
+    "bf16-pair-w-odd": _wl(109, (2, 8, 40), (2, 8, 8), 2, 128, "bf16"),    # nbt = nbh = 1, nbw = 5
+    "bf16-d64-bt128": _wl(110, (5, 12, 20), (2, 8, 8), 2, 64, "bf16"),
+    "bf16-block-4x4x4": _wl(111, (9, 10, 11), (4, 4, 4), 2, 128, "bf16"),
+    "f32-d64-bt128": _wl(112, (3, 9, 10), (2, 8, 8), 2, 64, "f32"),
 }
 
 
@@ -78,6 +85,10 @@ def test_small_full_parity(name):
     rows = range(wl.batch * wl.heads * geo.nb)
     print("max/mean err", compare_outputs(r["o"], o_ref, geo, rows, wl.heads, wl.dtype))
     assert r["tel"][:, 2].sum() == ci.size          # every kept tile done exactly once
+    # every schedule gives the same bits
+    for sched in (A.SCHED_NNZ_SORTED, A.SCHED_HEAD_MAJOR, A.SCHED_XCD_LOCAL):
+        o2 = _run(wl, p, wl.k_floor, sched=sched, inputs=(r["q"], r["k"], r["v"]))["o"]
+        assert np.array_equal(o2, r["o"])
 
 
 @pytest.mark.parametrize("name", ["bf16-d128-bt128-ragged", "f32-tiny-cfg0"])
@@ -215,6 +226,25 @@ def test_nan_input_keeps_mask_well_formed():
         cols = ci[rp[row]:rp[row + 1]]
         assert 1 <= cols.size <= geo.nb and (row % geo.nb) in cols
         assert (np.diff(cols) > 0).all()
+
+
+def test_maximum_blocks_per_head():
+    """nb = 4096, the largest the library accepts (16 x 16 x 16 blocks of
+    2 x 4 x 4 tokens): full mask check, sampled outputs."""
+    wl = _wl(113, (32, 64, 64), (2, 4, 4), 1, 64, "bf16", k_floor=3)
+    inputs = si.make_inputs(wl)
+    p = float(np.float32(0.9))
+    r = _run(wl, p, 3, inputs=inputs)
+    geo = O.geometry(wl.grid, wl.block)
+    assert geo.nb == 4096
+    q, k, v = (_np(t) for t in inputs)
+    res = O.route(q, k, geo, p, 3)
+    rp, ci = r["mask"].to_host()
+    keep = O.csr_to_keep(rp, ci, 1, 1, geo.nb)
+    print("mask rows", compare_masks(keep, res, p, 3))
+    rows = sample_rows(rp, 1, 1, geo.nb, geo, n_heads=1, n_blocks=24, seed=113)
+    o_ref = O.sparse_attention(q, k, v, geo, rp, ci, rows=rows)
+    print("max/mean err", compare_outputs(r["o"], o_ref, geo, rows, 1, "bf16"))
 
 
 # ---------------------------------------------------------------------------
