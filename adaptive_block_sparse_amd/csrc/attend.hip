@@ -274,8 +274,14 @@ __global__ void reset_counter_kernel(int* counter) {
 //     registers as the B operand, K_j read from LDS as the A operand);
 //   padding keys get -1e30 through one extra MFMA k-step (bias column times a
 //     ones row), so no per-element masking is needed;
-//   online softmax per query column: running max and sum in float32, exp2
-//     with log2(e)/sqrt(d) folded into one FMA;
+//   online softmax per query column: running sum in float32, exp2 with
+//     log2(e)/sqrt(d) folded into one FMA, and a lazily moved reference: a
+//     lane's reference moves to the chunk maximum only when that maximum
+//     exceeds it by more than 8 in the exp2 domain, otherwise the chunk's
+//     probabilities are taken against the old reference (at most 2^8, well
+//     inside bf16 and float range) and O^T needs no rescale; O^T and the sum
+//     stay relative to one common reference per query, so the result is the
+//     same softmax;
 //   O^T (d x queries) += Vt_j P^T, the probabilities converted to bf16 straight
 //     from the accumulator layout (see vt_perm).
 // K/V tiles are double buffered: the direct global->LDS copies of the next
@@ -489,6 +495,16 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
           if ((hc * C::CHS * 32) / (g.bh * g.bw) >= Tl) continue;
           // ---- S^T = K Q^T for the CHS key subtiles of this chunk
           f32x16_t s[C::CHS];
+          // K operands read from LDS 4 products ahead of use (the order of the
+          // reads and products is pinned)
+          constexpr int NQ = C::CHS * C::KS, PDK = 4 < NQ ? 4 : NQ;
+          auto kaddr = [&](int i) {
+            return reinterpret_cast<const bf16x8_t*>(kb + (i % C::KS) * (2 * BT * 16) +
+                                                     (hc * C::CHS + i / C::KS) * 512);
+          };
+          bf16x8_t kf[PDK];
+#pragma unroll
+          for (int i = 0; i < PDK; ++i) kf[i] = *kaddr(i);
 #pragma unroll
           for (int t2 = 0; t2 < C::CHS; ++t2) {
             const int t = hc * C::CHS + t2;
@@ -496,9 +512,11 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
             for (int e = 0; e < 16; ++e) s[t2][e] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
-              const bf16x8_t av =
-                  *reinterpret_cast<const bf16x8_t*>(kb + ks * (2 * BT * 16) + t * 512);
+              const int i = t2 * C::KS + ks;
+              const bf16x8_t av = kf[i % PDK];
+              if (i + PDK < NQ) kf[i % PDK] = *kaddr(i + PDK);
               s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qop[ks], s[t2], 0, 0, 0);
+              __builtin_amdgcn_sched_barrier(0);
             }
             if (partial) {
               // padding keys: add -1e30 through one extra k-step (bias column x ones row)
@@ -515,28 +533,40 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
           }
 
           // ---- online softmax over the chunk's keys, per query column
-          float mt = -INFINITY;
+          // four independent partial maxima (short dependency chains)
+          float mq[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mq[r] = s[0][r];
 #pragma unroll
           for (int t2 = 0; t2 < C::CHS; ++t2)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[t2][e]);
-          mt = fmaxf(mt, __shfl_xor(mt, 32));
-          const float m_new = fmaxf(m_run, mt);
-          const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-          const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * a.c);
-          const float mc = m_use * a.c;
+            for (int e = (t2 == 0 ? 4 : 0); e < 16; ++e) mq[e & 3] = fmaxf(mq[e & 3], s[t2][e]);
+          float mt = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+          {
+            // the other half of the query column lives in lane l ^ 32
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt),
+                                                             __float_as_uint(mt), false, false);
+            mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+          }
+          // lazily moved reference: only when the chunk maximum exceeds it by
+          // more than 8 in the exp2 domain (probabilities stay <= 2^8)
+          const bool up = !((mt - m_run) * a.c <= 8.0f);   // also true while m_run = -inf
+          const float m_new = up ? mt : m_run;
+          const float alpha = up ? __builtin_amdgcn_exp2f((m_run - m_new) * a.c) : 1.0f;
+          const float mc = m_new * a.c;
           bf16x8_t pop[2 * C::CHS];
-          float psum = 0.f;
+          float pq[4] = {0.f, 0.f, 0.f, 0.f};   // four independent partial sums
 #pragma unroll
           for (int t2 = 0; t2 < C::CHS; ++t2)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
               const float pv = __builtin_amdgcn_exp2f(fmaf(s[t2][e], a.c, -mc));
-              psum += pv;
+              pq[e & 3] += pv;
               pop[2 * t2 + e / 8][e % 8] = (__bf16)pv;
             }
+          const float psum = (pq[0] + pq[1]) + (pq[2] + pq[3]);
           l_run = l_run * alpha + psum;
-          if (m_new != m_run) {
+          if (up) {
 #pragma unroll
             for (int u = 0; u < C::DSUB; ++u)
 #pragma unroll
