@@ -206,9 +206,10 @@ def attend_run(plan: Plan, q, k, mask: Mask, o, sched: int, ws, telemetry=None,
                                          _stream(stream)))
 
 
-def attend(plan: Plan, q, k, v, mask: Mask, sched: int = SCHED_HEAD_PHASED, o=None, ws=None,
+def attend(plan: Plan, q, k, v, mask: Mask, sched: int = SCHED_XCD_LOCAL, o=None, ws=None,
            telemetry=None, stream=None):
-    """Block-sparse attention over the kept blocks; returns o [B, N, H, d]."""
+    """Block-sparse attention over the kept blocks; returns o [B, N, H, d].
+    The default queue places whole heads on XCDs (the fastest measured)."""
     torch = _check_qkv(plan, q, k, v)
     o = torch.empty_like(q) if o is None else o
     ws = workspace(plan.attend_ws_bytes, q.device) if ws is None else ws

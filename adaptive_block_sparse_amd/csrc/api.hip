@@ -76,9 +76,13 @@ AttendWs attend_ws_layout(const Geo& g, int dtype) {
   if (dtype == ABS_BF16) {
     L.kc = take((size_t)g.B * g.H * g.nb * g.Bt * g.d * 2);
     L.vc = take((size_t)g.B * g.H * g.nb * g.Bt * g.d * 2);
+    L.tlist = take((size_t)g.groups * tlist_cap(g) * sizeof(int));
+    L.tcount = take((size_t)g.groups * sizeof(int));
   } else {
     L.kc = take(0);
     L.vc = take((size_t)g.B * g.N * g.H * g.d * sizeof(float));
+    L.tlist = take(0);
+    L.tcount = take(0);
   }
   L.total = off;
   return L;
@@ -131,7 +135,7 @@ abs_status abs_plan_init(const abs_shape* shape, abs_plan* out) {
     p.padded[a] = p.nblk[a] * s.block[a];
     nb *= p.nblk[a];
   }
-  if (nb > 4096) return ABS_ENOTSUP;
+  if (nb > MAX_NB) return ABS_ENOTSUP;
   const long long tokens = (long long)s.grid[0] * s.grid[1] * s.grid[2];
   const long long rows = (long long)s.batch * s.heads * nb;
   // int32 indices: token offsets, CSR positions and element offsets per batch

@@ -153,11 +153,25 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
     const int heads = g.B * g.H;
     const bool lpt = heads <= MAX_LPT_HEADS;
     if (lpt) {
+      // every thread adds its items' costs to their heads (integer sums: the
+      // result does not depend on the order)
+      for (int hh = threadIdx.x; hh < heads; hh += NT) hcost[hh] = 0;
+      __syncthreads();
+      for (int it = threadIdx.x; it < items; it += NT)
+        atomicAdd(&hcost[it / g.groups_per_head], group_cost(g, row_ptr, it));
+    }
+    __syncthreads();
+    // heads in (cost desc, index asc) order: each thread ranks its heads
+    __shared__ int horder[MAX_LPT_HEADS];
+    if (lpt) {
       for (int hh = threadIdx.x; hh < heads; hh += NT) {
-        int c = 0;
-        for (int gl = 0; gl < g.groups_per_head; ++gl)
-          c += group_cost(g, row_ptr, hh * g.groups_per_head + gl);
-        hcost[hh] = c;
+        const int c = hcost[hh];
+        int r = 0;
+        for (int o = 0; o < heads; ++o) {
+          const int co = hcost[o];
+          r += (co > c || (co == c && o < hh)) ? 1 : 0;
+        }
+        horder[r] = hh;
       }
     }
     __syncthreads();
@@ -166,19 +180,12 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
       int rank[NXCD];
       for (int x = 0; x < NXCD; ++x) { load[x] = 0; rank[x] = 0; }
       for (int n = 0; n < heads && lpt; ++n) {
-        // next head in (cost desc, index asc) order; placed heads hold a
-        // negative cost
-        int best = -1;
-        for (int hh = 0; hh < heads; ++hh) {
-          if (hcost[hh] < 0) continue;
-          if (best < 0 || hcost[hh] > hcost[best]) best = hh;
-        }
+        const int best = horder[n];
         int xm = 0;
         for (int x = 1; x < NXCD; ++x)
           if (load[x] < load[xm]) xm = x;
         load[xm] += hcost[best];
         hbase[best] = xm * MAX_LPT_HEADS + rank[xm]++;   // (xcd, rank) packed
-        hcost[best] = -1 - hcost[best];                   // placed
       }
       for (int x = 0; x < NXCD; ++x) qlen[x] = 0;
       if (lpt) {
@@ -256,6 +263,78 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Per attention work item (a pair of query blocks of one head, or a single
+// block), the union of its rows' kept key-block lists in ascending order, each
+// entry j | (kept by the first block) << 17 | (kept by the second) << 18.  One
+// workgroup per item.  The two ascending lists are merged by rank: an element
+// of the first list goes to its index plus the number of elements of the
+// second list below it, an element of the second list to its index plus the
+// number of elements of the first list at or below it; the second copy of a
+// block both rows keep is marked, and a block-wide scan compacts the rest.
+// The list of item i starts at tlist[i * cap], cap = 2 nb, with tcount[i]
+// entries.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int rank_below(const int* x, int n, int v, bool inclusive) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const int xm = x[mid];
+    if (xm < v || (inclusive && xm == v)) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void tile_list_kernel(Geo g, const int* __restrict__ row_ptr,
+                                                        const int* __restrict__ col_idx, int cap,
+                                                        int* __restrict__ tlist,
+                                                        int* __restrict__ tcount) {
+  constexpr int NT = 256;
+  __shared__ int merged[2 * MAX_NB];   // j | owners << 17, or -1 for a dropped second copy
+  __shared__ int tmp[NT / 64 + 1];
+  const int item = blockIdx.x;
+  const int bhh = item / g.groups_per_head, gl = item % g.groups_per_head;
+  int lead, partner;
+  group_blocks(g, gl, &lead, &partner);
+  const int rA = bhh * g.nb + lead;
+  const int pA = row_ptr[rA], nA = row_ptr[rA + 1] - pA;
+  int pB = 0, nB = 0;
+  if (partner >= 0) {
+    const int rB = bhh * g.nb + partner;
+    pB = row_ptr[rB];
+    nB = row_ptr[rB + 1] - pB;
+  }
+  const int* A = col_idx + pA;
+  const int* Bl = col_idx + pB;
+  for (int i = threadIdx.x; i < nA; i += NT) {
+    const int v = A[i];
+    const int r = rank_below(Bl, nB, v, false);
+    const bool both = r < nB && Bl[r] == v;
+    merged[i + r] = v | ((both ? 3 : 1) << 17);
+  }
+  for (int i = threadIdx.x; i < nB; i += NT) {
+    const int v = Bl[i];
+    const int r = rank_below(A, nA, v, true);
+    const bool both = r > 0 && A[r - 1] == v;
+    merged[i + r] = both ? -1 : (v | (2 << 17));
+  }
+  __syncthreads();
+  const int n = nA + nB;
+  int* out = tlist + (long)item * cap;
+  int base = 0;
+  for (int e0 = 0; e0 < n; e0 += NT) {
+    const int e = e0 + threadIdx.x;
+    const int m = e < n ? merged[e] : -1;
+    int tot;
+    const int off = block_exclusive_scan<NT>(m >= 0 ? 1 : 0, tmp, &tot);
+    if (m >= 0) out[base + off] = m;
+    base += tot;
+  }
+  if (threadIdx.x == 0) tcount[item] = base;
+}
+
 __global__ void reset_counter_kernel(int* counter) {
   if (threadIdx.x == 0) counter[0] = 0;
   if (threadIdx.x < NXCD) counter[QHEAD + 32 * threadIdx.x] = 0;
@@ -265,7 +344,8 @@ __global__ void reset_counter_kernel(int* counter) {
 // bf16 block-sparse attention.  A workgroup handles one work item: a pair of
 // neighbouring query blocks of one head (or a single block), 4 waves per
 // query block (BT = 128), wave w owning query slots 32*(w%NW1) .. +31 of block
-// w/NW1.  The workgroup walks the union of the two ascending kept-block lists;
+// w/NW1.  The workgroup walks the union of the two ascending kept-block lists
+// (precomputed per item by tile_list_kernel and read two entries ahead);
 // each K/V tile is copied into LDS once and serves both blocks, which halves
 // the K/V traffic per flop (neighbouring blocks keep nearly the same key
 // blocks).  Per kept key block j, for the waves whose block keeps j, in chunks
@@ -316,6 +396,9 @@ struct AttnArgs {
   float c;  // log2(e) / sqrt(d)
   int head_major;
   int xcd_local;
+  const int* tlist;   // per item: union of the kept key blocks with owners (tile_list_kernel)
+  const int* tcount;  // per item: number of entries
+  int tlist_cap;      // entries reserved per item
 };
 
 typedef __attribute__((address_space(4))) const int cint_t;  // scalar-loadable
@@ -341,6 +424,10 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
   __shared__ __attribute__((aligned(1024))) char sV[2][C::TILE];
   __shared__ int s_off[BT];
   __shared__ int s_crd[BT];
+  // per key block: real extent Tl | Hl << 8 | Wl << 16, partial << 24 (128-token
+  // blocks; smaller blocks run two workgroups per CU and keep their LDS)
+  constexpr bool BINFO = BT == 128;
+  __shared__ int s_binfo[BINFO ? MAX_NB : 1];
   __shared__ int s_item;
 
   const Geo& g = a.g;
@@ -354,6 +441,15 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
     s_off[s] = (st * g.Hg + sh) * g.W + sw;
     s_crd[s] = st | (sh << 8) | (sw << 16);
   }
+  auto block_info = [&](int j) {
+    const int tb = j / (g.nbh * g.nbw), hb = (j / g.nbw) % g.nbh, wb = j % g.nbw;
+    const int Tl = min(g.bt, g.T - tb * g.bt), Hl = min(g.bh, g.Hg - hb * g.bh),
+              Wl = min(g.bw, g.W - wb * g.bw);
+    const int partial = (Tl < g.bt || Hl < g.bh || Wl < g.bw) ? 1 : 0;
+    return Tl | (Hl << 8) | (Wl << 16) | (partial << 24);
+  };
+  if constexpr (BINFO)
+    for (int j = tid; j < g.nb; j += C::NT) s_binfo[j] = block_info(j);
   __syncthreads();
 
   const uint32_t sK_base = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)&sK[0][0];
@@ -406,8 +502,6 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
     const int pA = ld_scalar(a.row_ptr, rA), nA = ld_scalar(a.row_ptr, rA + 1) - pA;
     const int pB = rB >= 0 ? ld_scalar(a.row_ptr, rB) : 0;
     const int nB = rB >= 0 ? ld_scalar(a.row_ptr, rB + 1) - pB : 0;
-    const int* colsA = a.col_idx + pA;
-    const int* colsB = a.col_idx + pB;
     const bool active = half == 0 || rB >= 0;     // this wave's query block exists
     const int iq = half == 0 ? lead : partner;
     const char* kc_head = (const char*)(a.kc + (long)bhh * g.nb * (D * BT));
@@ -428,12 +522,13 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
       }
     };
 
-    // merged walk over the two ascending lists
-    constexpr int END = 0x7fffffff;
-    int ia = 0, ib = 0;
-    int nxa = nA > 0 ? ld_scalar(colsA, 0) : END;
-    int nxb = nB > 0 ? ld_scalar(colsB, 0) : END;
-    issue(min(nxa, nxb), 0);
+    // walk over the item's precomputed union list, read two entries ahead
+    const int* tl = a.tlist + (long)item * a.tlist_cap;
+    const int nt = ld_scalar(a.tcount, item);
+    int e0 = nt > 0 ? ld_scalar(tl, 0) : -1;
+    int e1 = nt > 1 ? ld_scalar(tl, 1) : -1;
+    int e2 = nt > 2 ? ld_scalar(tl, 2) : -1;
+    if (e0 >= 0) issue(e0 & 0xffff, 0);
 
     // this lane's query slot
     const int tq = iq / (g.nbh * g.nbw), hq = (iq / g.nbw) % g.nbh, wqb = iq % g.nbw;
@@ -470,22 +565,22 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
     float m_run = -INFINITY, l_run = 0.f;
 
     int buf = 0;
-    while (nxa != END || nxb != END) {
-      const int j = min(nxa, nxb);
-      const bool needA = nxa == j, needB = nxb == j;
-      if (needA) { ++ia; nxa = ia < nA ? ld_scalar(colsA, ia) : END; }
-      if (needB) { ++ib; nxb = ib < nB ? ld_scalar(colsB, ib) : END; }
-      const int jn = min(nxa, nxb);
-      const bool mine = half == 0 ? needA : needB;
+    for (int t = 0; t < nt; ++t) {
+      const int j = e0 & 0xffff;
+      const bool mine = ((e0 >> (17 + half)) & 1) != 0;
+      const int jn = e1 >= 0 ? (e1 & 0xffff) : -1;
+      e0 = e1;
+      e1 = e2;
+      e2 = __builtin_amdgcn_readfirstlane(t + 3 < nt ? ld_scalar(tl, t + 3) : -1);
 
       wait_vmcnt<0>();      // this thread's copies of block j have landed
       wg_barrier();         // ... everyone's; and block j-1's buffer is free
-      if (jn != END) issue(jn, buf ^ 1);
+      if (jn >= 0) issue(jn, buf ^ 1);
 
       if (mine && wave_has_q) {
-        const int tb = j / (g.nbh * g.nbw), hb = (j / g.nbw) % g.nbh, wb = j % g.nbw;
-        const int Tl = g.T - tb * g.bt, Hl = g.Hg - hb * g.bh, Wl = g.W - wb * g.bw;
-        const bool partial = Tl < g.bt || Hl < g.bh || Wl < g.bw;
+        const int bi = __builtin_amdgcn_readfirstlane(BINFO ? s_binfo[j] : block_info(j));
+        const int Tl = bi & 255, Hl = (bi >> 8) & 255, Wl = (bi >> 16) & 255;
+        const bool partial = (bi >> 24) != 0;
         const char* kb = sK[buf] + kread;
         const char* vb = sV[buf] + vread;
 #pragma unroll
@@ -747,6 +842,9 @@ hipError_t launch_attend_prepare(const Geo& g, int dtype, const void* k, const v
     hipError_t e = hipMemcpyAsync(ws + L.vc, v, bytes, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
   }
+  if (dtype == ABS_BF16)
+    hipLaunchKernelGGL(tile_list_kernel, dim3(g.groups), dim3(256), 0, s, g, mask->row_ptr,
+                       mask->col_idx, tlist_cap(g), (int*)(ws + L.tlist), (int*)(ws + L.tcount));
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(512), 0, s, g, mask->row_ptr, sched,
                      heads_per_phase, (int*)(ws + L.sched), (int*)(ws + L.sort_a),
                      (int*)(ws + L.sort_b), (int*)(ws + L.counter));
@@ -825,6 +923,9 @@ hipError_t launch_attend_run(const Geo& g, int dtype, const void* q, const void*
     a.head_major = head_major ? 1 : 0;
     const bool persist = !head_major;
     a.xcd_local = sched == ABS_SCHED_XCD_LOCAL ? 1 : 0;
+    a.tlist = (const int*)(ws + L.tlist);
+    a.tcount = (const int*)(ws + L.tcount);
+    a.tlist_cap = tlist_cap(g);
     if (persist) hipLaunchKernelGGL(reset_counter_kernel, dim3(1), dim3(64), 0, s, a.counter);
     if (g.d == 128) {
       if (g.Bt == 128) launch_bf16<128, 128>(a, persist, grid, s);

@@ -65,6 +65,8 @@ struct AttendWs {
   size_t sort_a, sort_b;  // int32 [rows] each, radix-sort ping-pong
   size_t kc, vc;          // bf16: chunk-major K and V block tiles [B*H*nb*Bt*d] each;
                           // float32: vc holds a token-major copy of V, kc is empty
+  size_t tlist, tcount;   // bf16: per work item, the union of its rows' kept key
+                          // blocks with owners, int32 [groups * 2 nb], and the count [groups]
   size_t total;
 };
 
@@ -91,5 +93,7 @@ constexpr int NXCD = 8;          // XCDs (L2 domains) of an MI355X
 constexpr int QOFF = 32;         // counter[QOFF + x]: start of XCD queue x (x = 0..NXCD)
 constexpr int QHEAD = 64;        // counter[QHEAD + 32 x]: pull counter of XCD queue x
 constexpr int MAX_LPT_HEADS = 1024;
+constexpr int MAX_NB = 4096;     // key blocks per head supported by the plan
+inline int tlist_cap(const Geo& g) { return 2 * g.nb; }   // union entries per item
 
 }  // namespace abs_impl

@@ -52,7 +52,7 @@ def measured_traffic(workload_cfg: int, sched: str):
     import hashlib
     path = os.path.join(ROOT, "profiles", "attn_bf16_wan22_480p_hbm_traffic.md")
     src = os.path.join(ROOT, "adaptive_block_sparse_amd", "csrc", "attend.hip")
-    if workload_cfg != 1 or sched != "head_major" or not os.path.exists(path):
+    if workload_cfg != 1 or not os.path.exists(path):
         return None
     fields = {}
     for line in open(path):
@@ -60,7 +60,8 @@ def measured_traffic(workload_cfg: int, sched: str):
             key, _, val = line.partition(":")
             fields[key.strip()] = val.strip()
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if fields.get("attend_hip_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+    if (fields.get("attend_hip_sha256") != sha or fields.get("sched") != sched
+            or "traffic_bytes_per_launch" not in fields):
         return None
     return int(fields["traffic_bytes_per_launch"])
 
@@ -113,7 +114,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--p", type=float, default=None)
-    ap.add_argument("--sched", default="head_major",
+    ap.add_argument("--sched", default="xcd_local",
                     choices=["nnz_sorted", "head_major", "head_phased", "xcd_local"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--timed-only", action="store_true",
@@ -298,7 +299,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(eff_attn, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(eff_attn / peak, 4),
                      "traffic": measured_traffic(args.workload, args.sched),
-                     "kernel": "attn_bf16_kernel<128,128>",
+                     "kernel": ("attn_bf16_kernel<128,128,false>" if args.sched == "head_major"
+                                else "attn_bf16_kernel<128,128,true>"),
                      "per_unit": "4*Bt^2*d flop per kept tile"},
         "route_hbm": {"bytes_read_qk": 2 * wl.tokens * wl.heads * wl.head_dim * 2,
                       "gbs_algorithmic": round(2 * wl.tokens * wl.heads * wl.head_dim * 2
