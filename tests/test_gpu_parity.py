@@ -215,6 +215,34 @@ def test_pooled_means_and_schedule_array():
     np.testing.assert_array_equal(got, want)
 
 
+def test_wide_logit_range_moves_the_reference():
+    """Scores that climb by more than 2^8 (in exp2 units) from one key block to
+    the next, with every block kept: walking the blocks in ascending order, a
+    query's running reference must move at every block, so the kernel's
+    rescale path (taken only on jumps above 2^8) runs again and again.
+    Outputs still match the oracle."""
+    wl = SMALL["bf16-d128-bt128-ragged"]
+    geo = O.geometry(wl.grid, wl.block)
+    blk = np.full(wl.tokens, -1)
+    for j, mem in enumerate(O.block_members(geo)):
+        blk[mem[mem >= 0]] = j
+    rng = np.random.default_rng(2024)
+    q = np.zeros((1, wl.tokens, wl.heads, wl.head_dim), np.float32)
+    q[..., 0] = 8.0
+    k = (0.25 * rng.standard_normal(q.shape)).astype(np.float32)
+    k[..., 0] = 10.0 * blk[None, :, None]            # score 80 j: 10.2 exp2 units per block
+    v = rng.standard_normal(q.shape).astype(np.float32)
+    step = 8.0 * 10.0 * 1.4426950408889634 / np.sqrt(wl.head_dim)
+    assert step > 8.0
+    qt, kt, vt = (torch.from_numpy(x).to(torch.bfloat16) for x in (q, k, v))
+    r = _run(wl, 1.0, wl.k_floor, inputs=(qt, kt, vt), sched=A.SCHED_XCD_LOCAL)
+    rp, ci = r["mask"].to_host()
+    assert (np.diff(rp) == geo.nb).all()            # every block kept
+    o_ref = O.sparse_attention(_np(r["q"]), _np(r["k"]), _np(r["v"]), geo, rp, ci)
+    rows = range(wl.batch * wl.heads * geo.nb)
+    print("max/mean err", compare_outputs(r["o"], o_ref, geo, rows, wl.heads, wl.dtype))
+
+
 def test_nan_input_keeps_mask_well_formed():
     wl = SMALL["bf16-d128-bt128-ragged"]
     q, k, v = si.make_inputs(wl)
