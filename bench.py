@@ -12,6 +12,7 @@ timed region.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -114,6 +115,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--p", type=float, default=None)
+    ap.add_argument("--heads", type=int, default=None,
+                    help="run only the first H heads of the workload (one rank's share when "
+                         "the layer is sharded by head across GPUs)")
     ap.add_argument("--sched", default="xcd_local",
                     choices=["nnz_sorted", "head_major", "head_phased", "xcd_local"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -149,6 +153,11 @@ def main():
     import synth_inputs as si
 
     wl = si.WORKLOADS[args.workload]
+    if args.heads is not None:
+        if not 1 <= args.heads <= wl.heads:
+            print(f"--heads must be in 1..{wl.heads}", file=sys.stderr)
+            sys.exit(2)
+        wl = dataclasses.replace(wl, heads=args.heads, name=f"{wl.name}-first{args.heads}heads")
     p = float(np.float32(args.p if args.p is not None else wl.p[0]))
     sched = A.SCHEDULES[args.sched]
     print(f"[bench] generating {wl.name}", file=sys.stderr, flush=True)
