@@ -25,4 +25,7 @@ from .abs_oracle import (  # noqa: F401
     dense_attention,
     schedule,
     row_exemptions,
+    split_units,
+    partial_attention,
+    merge_partials,
 )

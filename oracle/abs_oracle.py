@@ -381,3 +381,79 @@ def schedule(costs, mode: str, items_per_head: Optional[int] = None,
         return np.array(sorted(range(n), key=lambda r: (phase[r], -costs[r], r)),
                         dtype=np.int64)
     raise ValueError(mode)
+
+
+# --------------------------------------------------------------------------
+# Split-and-merge: heavy work items cut into parts, parts merged by their lse
+# --------------------------------------------------------------------------
+def split_units(union_counts, split: int, max_parts: int):
+    """Cut heavy work items into parts for the split-and-merge attention.
+
+    Source: FVAttn explainer, part 2 (balance the work handed to each worker;
+    a single heavy head bounds how even that can be) and the APB-V paper notes
+    ("APB-V: Accelerating Long-Video Understanding via Sequence-Parallelism-aware
+    Approximate Attention"), key design 2: one query block's attention computed
+    in pieces on several hosts is joined through FlashAttention's log-sum-exp.
+    Reading on one GPU: a work item walks the ascending union of its rows' kept
+    key blocks (union_counts[i] entries); an item with nt > split entries
+    becomes P = ceil(nt / split) parts, part q taking entries
+    [q nt // P, (q + 1) nt // P); items are cut in item order while the running
+    sum of P over every such item so far (cut or not) stays within max_parts,
+    and each part owns the next result slot.
+
+    Returns (units, cut): units = [(item, t0, t1, slot)] in item order, slot -1
+    for an item left whole; cut = [(item, first_slot, P)].
+    """
+    units, cut = [], []
+    wanted = 0
+    slot = 0
+    for item, nt in enumerate(int(x) for x in union_counts):
+        parts = -(-nt // split) if nt > split else 1
+        if parts > 1:
+            wanted += parts
+            if wanted <= max_parts:
+                cut.append((item, slot, parts))
+                for q in range(parts):
+                    units.append((item, q * nt // parts, (q + 1) * nt // parts, slot + q))
+                slot += parts
+                continue
+        units.append((item, 0, nt, -1))
+    return units, cut
+
+
+def partial_attention(q, k, v):
+    """Softmax attention of queries q [n, d] over one part's keys k, v [m, d]:
+    (o [n, d], lse [n]) with o normalised over this part's keys and
+    lse = log sum_j exp(q . k_j / sqrt(d)) (natural log).  A part with no keys
+    gives o = 0 and lse = -inf.
+
+    Source: the APB-V paper notes, key design 2 (each host's partial attention
+    for the query block carries its log-sum-exp for the merge)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, d = q.shape
+    if k.shape[0] == 0:
+        return np.zeros((n, v.shape[1])), np.full(n, -np.inf)
+    s = q @ k.T / math.sqrt(d)
+    mx = s.max(axis=1, keepdims=True)
+    w = np.exp(s - mx)
+    tot = w.sum(axis=1, keepdims=True)
+    return (w / tot) @ v, (mx + np.log(tot))[:, 0]
+
+
+def merge_partials(parts):
+    """Join partial attentions over disjoint key sets: parts = [(o_p, lse_p)].
+    With L = log sum_p exp(lse_p), the result is sum_p exp(lse_p - L) o_p,
+    the attention over the union of the parts' keys.
+
+    Source: the APB-V paper notes, key design 2 (FlashAttention's log-sum-exp
+    merge of a query block's partial results)."""
+    lse = np.stack([np.asarray(l, dtype=np.float64) for _, l in parts])     # [P, n]
+    top = lse.max(axis=0)
+    if not np.isfinite(top).all():
+        raise ValueError("every query needs at least one key over the parts")
+    wts = np.exp(lse - top)                                                   # [P, n]
+    total = wts.sum(axis=0)
+    out = sum(w[:, None] * np.asarray(o, dtype=np.float64) for w, (o, _) in zip(wts, parts))
+    return out / total[:, None]
