@@ -28,7 +28,8 @@ SCHED_NNZ_SORTED, SCHED_HEAD_MAJOR, SCHED_HEAD_PHASED, SCHED_XCD_LOCAL = 0, 1, 2
 SCHEDULES = {"nnz_sorted": SCHED_NNZ_SORTED, "head_major": SCHED_HEAD_MAJOR,
              "head_phased": SCHED_HEAD_PHASED, "xcd_local": SCHED_XCD_LOCAL}
 EXPORTS = ("abs_plan_init", "abs_route", "abs_attend_prepare", "abs_attend_run",
-           "abs_attend", "abs_attend_grid", "abs_status_string")
+           "abs_attend", "abs_attend_grid", "abs_status_string", "abs_attend_split_ws_bytes",
+           "abs_attend_prepare_split", "abs_attend_run_split")
 
 
 class Shape(ctypes.Structure):
@@ -78,6 +79,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "abs_attend_run": [P, V, V, M, V, I32, V, SZ, V, V],
         "abs_attend": [P, V, V, V, M, V, I32, V, SZ, V, V],
         "abs_attend_grid": [P, I32, ctypes.POINTER(I32)],
+        "abs_attend_split_ws_bytes": [P, I32, ctypes.POINTER(SZ)],
+        "abs_attend_prepare_split": [P, V, V, M, I32, I32, I32, V, SZ, V],
+        "abs_attend_run_split": [P, V, M, V, I32, I32, V, SZ, V, V],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -215,4 +219,48 @@ def attend(plan: Plan, q, k, v, mask: Mask, sched: int = SCHED_XCD_LOCAL, o=None
     ws = workspace(plan.attend_ws_bytes, q.device) if ws is None else ws
     attend_prepare(plan, k, v, mask, sched, ws, stream)
     attend_run(plan, q, k, mask, o, sched, ws, telemetry, stream)
+    return o
+
+
+def attend_split_ws_bytes(plan: Plan, max_parts: int) -> int:
+    """Workspace bytes of the split-and-merge attention with max_parts slots."""
+    n = ctypes.c_size_t(0)
+    _check("abs_attend_split_ws_bytes",
+           load_library().abs_attend_split_ws_bytes(ctypes.byref(plan), int(max_parts),
+                                                    ctypes.byref(n)))
+    return int(n.value)
+
+
+def attend_prepare_split(plan: Plan, k, v, mask: Mask, sched: int, split_tiles: int,
+                         max_parts: int, ws, stream=None) -> None:
+    _check_qkv(plan, k, v)
+    cm = mask.c()
+    _check("abs_attend_prepare_split",
+           load_library().abs_attend_prepare_split(ctypes.byref(plan), _ptr(k), _ptr(v),
+                                                   ctypes.byref(cm), int(sched), int(split_tiles),
+                                                   int(max_parts), _ptr(ws), ws.numel(),
+                                                   _stream(stream)))
+
+
+def attend_run_split(plan: Plan, q, mask: Mask, o, sched: int, max_parts: int, ws,
+                     telemetry=None, stream=None) -> None:
+    _check_qkv(plan, q, o)
+    cm = mask.c()
+    tp = ctypes.c_void_p(0) if telemetry is None else _ptr(telemetry)
+    _check("abs_attend_run_split",
+           load_library().abs_attend_run_split(ctypes.byref(plan), _ptr(q), ctypes.byref(cm),
+                                               _ptr(o), int(sched), int(max_parts), _ptr(ws),
+                                               ws.numel(), tp, _stream(stream)))
+
+
+def attend_split(plan: Plan, q, k, v, mask: Mask, split_tiles: int, max_parts: int,
+                 sched: int = SCHED_NNZ_SORTED, o=None, ws=None, telemetry=None, stream=None):
+    """Block-sparse attention with heavy work items cut into parts of at most
+    about split_tiles union entries (at most max_parts parts in all), merged by
+    log-sum-exp; returns o [B, N, H, d]."""
+    torch = _check_qkv(plan, q, k, v)
+    o = torch.empty_like(q) if o is None else o
+    ws = workspace(attend_split_ws_bytes(plan, max_parts), q.device) if ws is None else ws
+    attend_prepare_split(plan, k, v, mask, sched, split_tiles, max_parts, ws, stream)
+    attend_run_split(plan, q, mask, o, sched, max_parts, ws, telemetry, stream)
     return o

@@ -65,14 +65,20 @@ RouteWs route_ws_layout(const Geo& g, bool slack) {
   return L;
 }
 
-AttendWs attend_ws_layout(const Geo& g, int dtype) {
+AttendWs attend_ws_layout(const Geo& g, int dtype, int max_parts) {
   AttendWs L;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
-  L.sched = take((size_t)g.rows * sizeof(int));
+  const bool split = max_parts >= 0;
+  const size_t queue = split ? (size_t)g.groups + (size_t)max_parts : (size_t)g.rows;
+  const size_t order = queue > (size_t)g.rows ? queue : (size_t)g.rows;
+  // split mode: the unit table comes first (its placement is part of the ABI)
+  L.units = split ? take(queue * 4 * sizeof(int)) : 0;
+  L.stab = split ? take((size_t)g.groups * 4 * sizeof(int)) : 0;
+  L.sched = take(order * sizeof(int));
   L.counter = take(512 * sizeof(int));
-  L.sort_a = take((size_t)g.rows * sizeof(int));
-  L.sort_b = take((size_t)g.rows * sizeof(int));
+  L.sort_a = take(order * sizeof(int));
+  L.sort_b = take(order * sizeof(int));
   if (dtype == ABS_BF16) {
     L.kc = take((size_t)g.B * g.H * g.nb * g.Bt * g.d * 2);
     L.vc = take((size_t)g.B * g.H * g.nb * g.Bt * g.d * 2);
@@ -84,6 +90,7 @@ AttendWs attend_ws_layout(const Geo& g, int dtype) {
     L.tlist = take(0);
     L.tcount = take(0);
   }
+  L.part = take(split ? (size_t)max_parts * part_floats(g) * sizeof(float) : 0);
   L.total = off;
   return L;
 }
@@ -221,6 +228,55 @@ abs_status abs_attend(const abs_plan* plan, const void* q, const void* k, const 
   abs_status st = abs_attend_prepare(plan, k, v, mask, sched, ws, ws_bytes, stream);
   if (st != ABS_OK) return st;
   return abs_attend_run(plan, q, k, mask, o, sched, ws, ws_bytes, telemetry, stream);
+}
+
+// split-and-merge entry points: persistent sorted queues, bf16 only
+static abs_status split_args(const abs_plan* plan, int32_t sched, int32_t max_parts) {
+  if (!plan_ok(plan)) return ABS_EINVAL;
+  if (sched != ABS_SCHED_NNZ_SORTED && sched != ABS_SCHED_HEAD_PHASED) return ABS_EINVAL;
+  if (max_parts < 0 || max_parts > MAX_SPLIT_PARTS) return ABS_EINVAL;
+  if (plan->s.dtype != ABS_BF16) return ABS_ENOTSUP;
+  return ABS_OK;
+}
+
+abs_status abs_attend_split_ws_bytes(const abs_plan* plan, int32_t max_parts, size_t* bytes) {
+  if (!bytes) return ABS_EINVAL;
+  const abs_status st = split_args(plan, ABS_SCHED_NNZ_SORTED, max_parts);
+  if (st != ABS_OK) return st;
+  *bytes = attend_ws_layout(make_geo(plan), plan->s.dtype, max_parts).total;
+  return ABS_OK;
+}
+
+abs_status abs_attend_prepare_split(const abs_plan* plan, const void* k, const void* v,
+                                    const abs_mask* mask, int32_t sched, int32_t split_tiles,
+                                    int32_t max_parts, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan_ok(plan) || !k || !v || !mask_ok(mask) || !ws) return ABS_EINVAL;
+  if (split_tiles < 1) return ABS_EINVAL;
+  const abs_status st = split_args(plan, sched, max_parts);
+  if (st != ABS_OK) return st;
+  Geo g = make_geo(plan);
+  AttendWs L = attend_ws_layout(g, plan->s.dtype, max_parts);
+  if (ws_bytes < L.total) return ABS_ENOSPACE;
+  hipError_t e = launch_attend_prepare_split(g, k, v, mask, sched, plan->heads_per_phase,
+                                             split_tiles, max_parts, (char*)ws, L,
+                                             (hipStream_t)stream);
+  return e == hipSuccess ? ABS_OK : ABS_EHIP;
+}
+
+abs_status abs_attend_run_split(const abs_plan* plan, const void* q, const abs_mask* mask,
+                                void* o, int32_t sched, int32_t max_parts, void* ws,
+                                size_t ws_bytes, int64_t* telemetry, void* stream) {
+  if (!plan_ok(plan) || !q || !o || !mask_ok(mask) || !ws) return ABS_EINVAL;
+  const abs_status st = split_args(plan, sched, max_parts);
+  if (st != ABS_OK) return st;
+  Geo g = make_geo(plan);
+  AttendWs L = attend_ws_layout(g, plan->s.dtype, max_parts);
+  if (ws_bytes < L.total) return ABS_ENOSPACE;
+  const int grid = attend_grid(g, plan->s.dtype, sched);
+  if (grid <= 0) return ABS_EHIP;
+  hipError_t e = launch_attend_run_split(g, q, mask, o, max_parts, (char*)ws, L, telemetry, grid,
+                                         (hipStream_t)stream);
+  return e == hipSuccess ? ABS_OK : ABS_EHIP;
 }
 
 }  // extern "C"

@@ -122,9 +122,19 @@ __device__ __forceinline__ int group_cost(const Geo& g, const int* row_ptr, int 
   return c;
 }
 
-__device__ __forceinline__ unsigned sched_key(const Geo& g, const int* row_ptr, int item,
-                                              int phased, int hpp) {
-  const unsigned k = (unsigned)(2 * g.nb - group_cost(g, row_ptr, item));
+// Key of queue entry r: a work item, or (split-and-merge) a work unit whose
+// cost is the length of its range of the item's union list (at most 2nb).
+__device__ __forceinline__ unsigned sched_key(const Geo& g, const int* row_ptr, const int* units,
+                                              int r, int phased, int hpp) {
+  int item, cost;
+  if (units) {
+    item = units[4 * r];
+    cost = units[4 * r + 2] - units[4 * r + 1];
+  } else {
+    item = r;
+    cost = group_cost(g, row_ptr, r);
+  }
+  const unsigned k = (unsigned)(2 * g.nb - cost);
   return phased ? (unsigned)((item / g.groups_per_head) / hpp) * (unsigned)(2 * g.nb + 1) + k : k;
 }
 
@@ -132,11 +142,13 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
                                                        int mode, int hpp, int* __restrict__ sched,
                                                        int* __restrict__ buf_a,
                                                        int* __restrict__ buf_b,
-                                                       int* __restrict__ counter) {
+                                                       int* __restrict__ counter,
+                                                       const int* __restrict__ units) {
   constexpr int NT = 512;
   __shared__ unsigned offs[16][NT];
   __shared__ unsigned stmp[NT / 64 + 1];
-  const int items = g.groups;
+  // queue entries: work items, or the split units counted by split_units_kernel
+  const int items = units ? counter[NUNITS] : g.groups;
   if (threadIdx.x == 0) counter[0] = 0;
   if (threadIdx.x < NXCD) counter[QHEAD + 32 * threadIdx.x] = 0;
   if (mode == ABS_SCHED_HEAD_MAJOR) {
@@ -228,7 +240,7 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
     for (int x = 0; x < 16; ++x) cnt[x] = 0u;
     for (int e = lo; e < hi; ++e) {
       const int r = src ? src[e] : e;
-      const unsigned dg = (sched_key(g, row_ptr, r, phased, hpp) >> sh) & 15u;
+      const unsigned dg = (sched_key(g, row_ptr, units, r, phased, hpp) >> sh) & 15u;
 #pragma unroll
       for (int x = 0; x < 16; ++x) cnt[x] += (dg == (unsigned)x) ? 1u : 0u;
     }
@@ -255,7 +267,7 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
     __syncthreads();
     for (int e = lo; e < hi; ++e) {
       const int r = src ? src[e] : e;
-      const unsigned dg = (sched_key(g, row_ptr, r, phased, hpp) >> sh) & 15u;
+      const unsigned dg = (sched_key(g, row_ptr, units, r, phased, hpp) >> sh) & 15u;
       const unsigned pos = offs[dg][threadIdx.x]++;
       dst[pos] = r;
     }
@@ -335,6 +347,64 @@ __global__ __launch_bounds__(256) void tile_list_kernel(Geo g, const int* __rest
   if (threadIdx.x == 0) tcount[item] = base;
 }
 
+// ---------------------------------------------------------------------------
+// Split-and-merge queue (one workgroup).  A work item whose union list holds
+// nt > split entries is cut into P = ceil(nt / split) parts, part p covering
+// entries [p nt / P, (p+1) nt / P) (integer division, every part non-empty),
+// as long as the running total of parts over all such items up to and
+// including it, in item order, stays within max_parts (that total only grows,
+// so the items cut are a prefix of the heavy ones).  Each part owns one partial-result slot; an
+// item that is not cut is one unit that writes its output directly.
+//   units[u] = {item, t0, t1, slot or -1}, units of an item consecutive, items
+//              in order;
+//   stab[s]  = {item, first slot, P, 0} for the s-th item that is cut;
+//   counter[NUNITS], counter[NSPLIT] = number of units, of cut items.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void split_units_kernel(Geo g, const int* __restrict__ tcount,
+                                                           int split, int max_parts,
+                                                           int4* __restrict__ units,
+                                                           int4* __restrict__ stab,
+                                                           int* __restrict__ counter) {
+  constexpr int NT = 1024;
+  __shared__ int tmp[NT / 64 + 1];
+  int want_base = 0, slot_base = 0, unit_base = 0, split_base = 0;
+  for (int i0 = 0; i0 < g.groups; i0 += NT) {
+    const int i = i0 + threadIdx.x;
+    int nt = 0, P = 1;
+    if (i < g.groups) {
+      nt = tcount[i];
+      P = nt > split ? (nt + split - 1) / split : 1;
+    }
+    const int want = P > 1 ? P : 0;
+    int tot;
+    const int wpre = block_exclusive_scan<NT>(want, tmp, &tot);
+    const bool cut = want > 0 && want_base + wpre + want <= max_parts;
+    const int nu = i < g.groups ? (cut ? P : 1) : 0;
+    int utot, stot, ctot;
+    const int upre = block_exclusive_scan<NT>(nu, tmp, &utot);
+    const int spre = block_exclusive_scan<NT>(cut ? 1 : 0, tmp, &stot);
+    const int cpre = block_exclusive_scan<NT>(cut ? P : 0, tmp, &ctot);
+    if (i < g.groups) {
+      const int u0 = unit_base + upre, slot0 = slot_base + cpre;
+      if (cut) {
+        for (int q = 0; q < P; ++q)
+          units[u0 + q] = make_int4(i, (q * nt) / P, ((q + 1) * nt) / P, slot0 + q);
+        stab[split_base + spre] = make_int4(i, slot0, P, 0);
+      } else {
+        units[u0] = make_int4(i, 0, nt, -1);
+      }
+    }
+    want_base += tot;
+    slot_base += ctot;
+    unit_base += utot;
+    split_base += stot;
+  }
+  if (threadIdx.x == 0) {
+    counter[NUNITS] = unit_base;
+    counter[NSPLIT] = split_base;
+  }
+}
+
 __global__ void reset_counter_kernel(int* counter) {
   if (threadIdx.x == 0) counter[0] = 0;
   if (threadIdx.x < NXCD) counter[QHEAD + 32 * threadIdx.x] = 0;
@@ -399,6 +469,10 @@ struct AttnArgs {
   const int* tlist;   // per item: union of the kept key blocks with owners (tile_list_kernel)
   const int* tcount;  // per item: number of entries
   int tlist_cap;      // entries reserved per item
+  // split-and-merge mode: queue entries are units {item, t0, t1, slot}
+  const int* units;
+  float* part;        // partial-result slots
+  long part_floats;   // floats per slot
 };
 
 typedef __attribute__((address_space(4))) const int cint_t;  // scalar-loadable
@@ -417,8 +491,9 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
                : "memory", "m0");
 }
 
-template <int D, int BT, bool PERSIST>
+template <int D, int BT, bool PERSIST, bool SPLIT = false>
 __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs a) {
+  static_assert(PERSIST || !SPLIT, "split units come from the persistent queue");
   using C = AttnCfg<D, BT>;
   __shared__ __attribute__((aligned(1024))) char sK[2][C::TILE];
   __shared__ __attribute__((aligned(1024))) char sV[2][C::TILE];
@@ -460,6 +535,8 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
   const long long t_start = (long long)wall_clock64();
   long long tiles = 0;
 
+  // queue length: work items, or the split units (written by the prologue)
+  const int qlen = SPLIT ? ld_scalar(a.counter, NUNITS) : g.groups;
   int iter = 0;
   while (true) {
     int item;
@@ -483,7 +560,7 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
       }
       __syncthreads();
       item = __builtin_amdgcn_readfirstlane(s_item);
-      if (item >= g.groups) break;
+      if (item >= qlen) break;
       item = ld_scalar(a.sched, item);
     } else {
       if (iter > 0) break;
@@ -491,6 +568,16 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
     }
     ++iter;
     item = __builtin_amdgcn_readfirstlane(item);
+    // split-and-merge: this unit covers entries [t0, t1) of the item's list and
+    // writes its partial result to a slot (slot < 0: the whole item, final output)
+    int t0 = 0, t1 = 0, slot = -1;
+    if constexpr (SPLIT) {
+      const int u = item;
+      item = __builtin_amdgcn_readfirstlane(ld_scalar(a.units, 4l * u));
+      t0 = __builtin_amdgcn_readfirstlane(ld_scalar(a.units, 4l * u + 1));
+      t1 = __builtin_amdgcn_readfirstlane(ld_scalar(a.units, 4l * u + 2));
+      slot = __builtin_amdgcn_readfirstlane(ld_scalar(a.units, 4l * u + 3));
+    }
 
     const int bhh = item / g.groups_per_head, gl = item % g.groups_per_head;
     int lead, partner;
@@ -523,8 +610,8 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
     };
 
     // walk over the item's precomputed union list, read two entries ahead
-    const int* tl = a.tlist + (long)item * a.tlist_cap;
-    const int nt = ld_scalar(a.tcount, item);
+    const int* tl = a.tlist + (long)item * a.tlist_cap + t0;
+    const int nt = SPLIT ? t1 - t0 : ld_scalar(a.tcount, item);
     int e0 = nt > 0 ? ld_scalar(tl, 0) : -1;
     int e1 = nt > 1 ? ld_scalar(tl, 1) : -1;
     int e2 = nt > 2 ? ld_scalar(tl, 2) : -1;
@@ -569,6 +656,7 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
       const int j = e0 & 0xffff;
       const bool mine = ((e0 >> (17 + half)) & 1) != 0;
       const int jn = e1 >= 0 ? (e1 & 0xffff) : -1;
+      if constexpr (SPLIT) tiles += ((e0 >> 17) & 1) + ((e0 >> 18) & 1);   // owned tiles
       e0 = e1;
       e1 = e2;
       e2 = __builtin_amdgcn_readfirstlane(t + 3 < nt ? ld_scalar(tl, t + 3) : -1);
@@ -684,12 +772,28 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
       }
       buf ^= 1;
     }
-    tiles += nA + nB;
+    if constexpr (!SPLIT) tiles += nA + nB;
 
     // ---- epilogue: normalise and store the real query rows
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    if (qvalid) {
+    if (SPLIT && slot >= 0) {
+      // partial result of this part, every query slot of the pair: O^T relative
+      // to the reference m (not normalised), m in the exp2 domain, and the sum
+      float* ps = a.part + (long)slot * a.part_floats;
+      const int qi = half * BT + qs;
+      float* prow = ps + (long)qi * D + 4 * hf;
+#pragma unroll
+      for (int u = 0; u < C::DSUB; ++u)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<float4*>(prow + 32 * u + 8 * g4) =
+              make_float4(o[u][4 * g4 + 0], o[u][4 * g4 + 1], o[u][4 * g4 + 2], o[u][4 * g4 + 3]);
+      if (hf == 0) {
+        ps[2 * BT * D + qi] = m_run * a.c;
+        ps[2 * BT * D + 2 * BT + qi] = l_tot;
+      }
+    } else if (qvalid) {
       bf16_t* orow = a.o + ((tok_base + nq) * g.H + h) * D + 4 * hf;
 #pragma unroll
       for (int u = 0; u < C::DSUB; ++u)
@@ -712,6 +816,70 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
     t[1] = (long long)xcc_id_reg();
     t[2] = tiles;
     t[3] = (long long)wall_clock64() - t_start;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the parts of every cut work item (one workgroup per cut item).
+// Part p left, per query, O_p = sum over its keys of 2^(c s - m_p) v, its sum
+// l_p and its reference m_p (exp2 domain, -inf when the part had no key of the
+// query's row).  With M = max_p m_p and weights w_p = 2^(m_p - M), the
+// softmax over the union of the parts' keys is
+//   O = (sum_p w_p O_p) / (sum_p w_p l_p),
+// the same log-sum-exp combination as merging attention computed over
+// disjoint key sets.  Parts are combined in ascending order, so the result does
+// not depend on the schedule.  Thread f handles 4 consecutive d of one query.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void merge_parts_kernel(Geo g, const int* __restrict__ stab,
+                                                          const int* __restrict__ counter,
+                                                          const float* __restrict__ part,
+                                                          long pf, bf16_t* __restrict__ o) {
+  const int sidx = blockIdx.x;
+  if (sidx >= counter[NSPLIT]) return;
+  const int item = stab[4 * sidx], slot0 = stab[4 * sidx + 1], P = stab[4 * sidx + 2];
+  const int bhh = item / g.groups_per_head, gl = item % g.groups_per_head;
+  int lead, partner;
+  group_blocks(g, gl, &lead, &partner);
+  const int b = bhh / g.H, h = bhh % g.H;
+  const int BT = g.Bt, D = g.d, C4 = D / 4;
+  const float* base = part + (long)slot0 * pf;
+  const long mo = 2l * BT * D, lo = mo + 2 * BT;
+  const int plane = g.bh * g.bw;
+  for (int f = threadIdx.x; f < 2 * BT * C4; f += blockDim.x) {
+    const int qi = f / C4, c4 = f % C4;
+    const int half = qi / BT, qs = qi % BT;
+    const int blk = half ? partner : lead;
+    if (blk < 0) continue;
+    const int tb = blk / (g.nbh * g.nbw), hb = (blk / g.nbw) % g.nbh, wb = blk % g.nbw;
+    const int tt = tb * g.bt + qs / plane, hh = hb * g.bh + (qs / g.bw) % g.bh,
+              ww = wb * g.bw + qs % g.bw;
+    if (tt >= g.T || hh >= g.Hg || ww >= g.W) continue;   // padding slot: no output
+    const long n = ((long)tt * g.Hg + hh) * g.W + ww;
+    float M = -INFINITY;
+    for (int p = 0; p < P; ++p) M = fmaxf(M, base[p * pf + mo + qi]);
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (M > -INFINITY) {
+      for (int p = 0; p < P; ++p) {
+        const float* sp = base + p * pf;
+        const float wgt = __builtin_amdgcn_exp2f(sp[mo + qi] - M);
+        L = fmaf(wgt, sp[lo + qi], L);
+        const float4 v = *reinterpret_cast<const float4*>(sp + (long)qi * D + 4 * c4);
+        acc.x = fmaf(wgt, v.x, acc.x);
+        acc.y = fmaf(wgt, v.y, acc.y);
+        acc.z = fmaf(wgt, v.z, acc.z);
+        acc.w = fmaf(wgt, v.w, acc.w);
+      }
+    }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    const __bf16 v0 = (__bf16)(acc.x * inv), v1 = (__bf16)(acc.y * inv);
+    const __bf16 v2 = (__bf16)(acc.z * inv), v3 = (__bf16)(acc.w * inv);
+    const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
+    const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, v2) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
+    *reinterpret_cast<uint2*>(o + (((long)b * g.N + n) * g.H + h) * D + 4 * c4) =
+        make_uint2(w0, w1);
   }
 }
 
@@ -821,21 +989,26 @@ static void launch_relayout(const Geo& g, const void* k, const void* v, bf16_t* 
                      (const bf16_t*)k, (const bf16_t*)v, kc, vc);
 }
 
+static void launch_relayout_bf16(const Geo& g, const void* k, const void* v, char* ws,
+                                 const AttendWs& L, hipStream_t s) {
+  bf16_t* kc = (bf16_t*)(ws + L.kc);
+  bf16_t* vc = (bf16_t*)(ws + L.vc);
+  if (g.d == 128) {
+    if (g.Bt == 128) launch_relayout<128, 128>(g, k, v, kc, vc, s);
+    else if (g.Bt == 64) launch_relayout<128, 64>(g, k, v, kc, vc, s);
+    else launch_relayout<128, 32>(g, k, v, kc, vc, s);
+  } else {
+    if (g.Bt == 128) launch_relayout<64, 128>(g, k, v, kc, vc, s);
+    else if (g.Bt == 64) launch_relayout<64, 64>(g, k, v, kc, vc, s);
+    else launch_relayout<64, 32>(g, k, v, kc, vc, s);
+  }
+}
+
 hipError_t launch_attend_prepare(const Geo& g, int dtype, const void* k, const void* v,
                                  const abs_mask* mask, int sched, int heads_per_phase, char* ws,
                                  const AttendWs& L, hipStream_t s) {
   if (dtype == ABS_BF16) {
-    bf16_t* kc = (bf16_t*)(ws + L.kc);
-    bf16_t* vc = (bf16_t*)(ws + L.vc);
-    if (g.d == 128) {
-      if (g.Bt == 128) launch_relayout<128, 128>(g, k, v, kc, vc, s);
-      else if (g.Bt == 64) launch_relayout<128, 64>(g, k, v, kc, vc, s);
-      else launch_relayout<128, 32>(g, k, v, kc, vc, s);
-    } else {
-      if (g.Bt == 128) launch_relayout<64, 128>(g, k, v, kc, vc, s);
-      else if (g.Bt == 64) launch_relayout<64, 64>(g, k, v, kc, vc, s);
-      else launch_relayout<64, 32>(g, k, v, kc, vc, s);
-    }
+    launch_relayout_bf16(g, k, v, ws, L, s);
   } else {
     // float32 path: the attention kernel reads V token-major from the workspace
     const size_t bytes = (size_t)g.B * g.N * g.H * g.d * sizeof(float);
@@ -847,14 +1020,26 @@ hipError_t launch_attend_prepare(const Geo& g, int dtype, const void* k, const v
                        mask->col_idx, tlist_cap(g), (int*)(ws + L.tlist), (int*)(ws + L.tcount));
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(512), 0, s, g, mask->row_ptr, sched,
                      heads_per_phase, (int*)(ws + L.sched), (int*)(ws + L.sort_a),
-                     (int*)(ws + L.sort_b), (int*)(ws + L.counter));
+                     (int*)(ws + L.sort_b), (int*)(ws + L.counter), (const int*)nullptr);
   return hipGetLastError();
 }
 
-template <int D, int BT, bool P>
-static const void* bf16_kernel_ptr() {
-  return reinterpret_cast<const void*>(&attn_bf16_kernel<D, BT, P>);
+hipError_t launch_attend_prepare_split(const Geo& g, const void* k, const void* v,
+                                       const abs_mask* mask, int sched, int heads_per_phase,
+                                       int split_tiles, int max_parts, char* ws,
+                                       const AttendWs& L, hipStream_t s) {
+  launch_relayout_bf16(g, k, v, ws, L, s);
+  hipLaunchKernelGGL(tile_list_kernel, dim3(g.groups), dim3(256), 0, s, g, mask->row_ptr,
+                     mask->col_idx, tlist_cap(g), (int*)(ws + L.tlist), (int*)(ws + L.tcount));
+  hipLaunchKernelGGL(split_units_kernel, dim3(1), dim3(1024), 0, s, g, (const int*)(ws + L.tcount),
+                     split_tiles, max_parts, (int4*)(ws + L.units), (int4*)(ws + L.stab),
+                     (int*)(ws + L.counter));
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(512), 0, s, g, mask->row_ptr, sched,
+                     heads_per_phase, (int*)(ws + L.sched), (int*)(ws + L.sort_a),
+                     (int*)(ws + L.sort_b), (int*)(ws + L.counter), (const int*)(ws + L.units));
+  return hipGetLastError();
 }
+
 
 template <int D, int BT>
 static int persistent_grid() {
@@ -902,13 +1087,18 @@ static void launch_bf16(const AttnArgs& a, bool persist, int grid, hipStream_t s
     hipLaunchKernelGGL((attn_bf16_kernel<D, BT, false>), dim3(grid), dim3(4 * BT), 0, s, a);
 }
 
+template <int D, int BT>
+static void launch_bf16_split(const AttnArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((attn_bf16_kernel<D, BT, true, true>), dim3(grid), dim3(4 * BT), 0, s, a);
+}
+
 hipError_t launch_attend_run(const Geo& g, int dtype, const void* q, const void* k,
                              const abs_mask* mask, void* o, int sched, char* ws,
                              const AttendWs& L, int64_t* telemetry, int grid, hipStream_t s) {
   const int* sch = (const int*)(ws + L.sched);
   const bool head_major = sched == ABS_SCHED_HEAD_MAJOR;
   if (dtype == ABS_BF16) {
-    AttnArgs a;
+    AttnArgs a = {};
     a.g = g;
     a.q = (const bf16_t*)q;
     a.kc = (const bf16_t*)(ws + L.kc);
@@ -947,6 +1137,46 @@ hipError_t launch_attend_run(const Geo& g, int dtype, const void* q, const void*
                          (const float*)k, (const float*)(ws + L.vc), mask->row_ptr, mask->col_idx,
                          sch, head_major ? 1 : 0, (float*)o, (long long*)telemetry, scale);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_run_split(const Geo& g, const void* q, const abs_mask* mask, void* o,
+                                   int max_parts, char* ws, const AttendWs& L,
+                                   int64_t* telemetry, int grid, hipStream_t s) {
+  AttnArgs a = {};
+  a.g = g;
+  a.q = (const bf16_t*)q;
+  a.kc = (const bf16_t*)(ws + L.kc);
+  a.vc = (const bf16_t*)(ws + L.vc);
+  a.row_ptr = mask->row_ptr;
+  a.col_idx = mask->col_idx;
+  a.sched = (const int*)(ws + L.sched);
+  a.counter = (int*)(ws + L.counter);
+  a.o = (bf16_t*)o;
+  a.telem = (long long*)telemetry;
+  a.c = (float)(1.4426950408889634 / sqrt((double)g.d));
+  a.tlist = (const int*)(ws + L.tlist);
+  a.tcount = (const int*)(ws + L.tcount);
+  a.tlist_cap = tlist_cap(g);
+  a.units = (const int*)(ws + L.units);
+  a.part = (float*)(ws + L.part);
+  a.part_floats = (long)part_floats(g);
+  hipLaunchKernelGGL(reset_counter_kernel, dim3(1), dim3(64), 0, s, a.counter);
+  if (g.d == 128) {
+    if (g.Bt == 128) launch_bf16_split<128, 128>(a, grid, s);
+    else if (g.Bt == 64) launch_bf16_split<128, 64>(a, grid, s);
+    else launch_bf16_split<128, 32>(a, grid, s);
+  } else {
+    if (g.Bt == 128) launch_bf16_split<64, 128>(a, grid, s);
+    else if (g.Bt == 64) launch_bf16_split<64, 64>(a, grid, s);
+    else launch_bf16_split<64, 32>(a, grid, s);
+  }
+  // every cut item has at least two parts
+  const long most = (long)max_parts / 2 < (long)g.groups ? (long)max_parts / 2 : (long)g.groups;
+  if (most > 0)
+    hipLaunchKernelGGL(merge_parts_kernel, dim3((unsigned)most), dim3(256), 0, s, g,
+                       (const int*)(ws + L.stab), (const int*)(ws + L.counter),
+                       (const float*)(ws + L.part), (long)part_floats(g), (bf16_t*)o);
   return hipGetLastError();
 }
 

@@ -59,20 +59,26 @@ struct RouteWs {
 
 // Attend workspace layout.
 struct AttendWs {
-  size_t sched;           // int32 [rows]
+  size_t sched;           // int32 [rows], or [groups + max_parts] work units when split
   size_t counter;         // int32 [512]: [0] queue head; [32..40] XCD queue offsets;
                           // [64 + 32x] head of XCD queue x (own cache line each)
-  size_t sort_a, sort_b;  // int32 [rows] each, radix-sort ping-pong
+  size_t sort_a, sort_b;  // int32, as sched, radix-sort ping-pong
   size_t kc, vc;          // bf16: chunk-major K and V block tiles [B*H*nb*Bt*d] each;
                           // float32: vc holds a token-major copy of V, kc is empty
   size_t tlist, tcount;   // bf16: per work item, the union of its rows' kept key
                           // blocks with owners, int32 [groups * 2 nb], and the count [groups]
+  // split-and-merge mode only (sizes 0 otherwise):
+  size_t units;           // int4 [groups + max_parts]: {item, t0, t1, slot or -1}
+  size_t stab;            // int4 [groups]: per split item {item, first slot, parts, 0}
+  size_t part;            // float32 slots [max_parts]: partial O^T [2][Bt][d], m [2][Bt],
+                          // l [2][Bt] (see part_floats)
   size_t total;
 };
 
 Geo make_geo(const abs_plan* plan);
 RouteWs route_ws_layout(const Geo& g, bool slack);
-AttendWs attend_ws_layout(const Geo& g, int dtype);
+// max_parts < 0: the plain layout; >= 0: with the split-and-merge buffers
+AttendWs attend_ws_layout(const Geo& g, int dtype, int max_parts = -1);
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_route(const Geo& g, int dtype, const void* q, const void* k, float p,
@@ -85,6 +91,15 @@ hipError_t launch_attend_prepare(const Geo& g, int dtype, const void* k, const v
 hipError_t launch_attend_run(const Geo& g, int dtype, const void* q, const void* k,
                              const abs_mask* mask, void* o, int sched, char* ws,
                              const AttendWs& L, int64_t* telemetry, int grid, hipStream_t s);
+// Split-and-merge variants (bf16): heavy work items cut into parts along their
+// union tile lists, partial results merged by log-sum-exp weights.
+hipError_t launch_attend_prepare_split(const Geo& g, const void* k, const void* v,
+                                       const abs_mask* mask, int sched, int heads_per_phase,
+                                       int split_tiles, int max_parts, char* ws,
+                                       const AttendWs& L, hipStream_t s);
+hipError_t launch_attend_run_split(const Geo& g, const void* q, const abs_mask* mask, void* o,
+                                   int max_parts, char* ws, const AttendWs& L,
+                                   int64_t* telemetry, int grid, hipStream_t s);
 int attend_grid(const Geo& g, int dtype, int sched);
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -93,7 +108,13 @@ constexpr int NXCD = 8;          // XCDs (L2 domains) of an MI355X
 constexpr int QOFF = 32;         // counter[QOFF + x]: start of XCD queue x (x = 0..NXCD)
 constexpr int QHEAD = 64;        // counter[QHEAD + 32 x]: pull counter of XCD queue x
 constexpr int MAX_LPT_HEADS = 1024;
+constexpr int NUNITS = 48;       // counter[NUNITS]: work units of the split-and-merge queue
+constexpr int NSPLIT = 49;       // counter[NSPLIT]: items cut into two or more parts
+constexpr int MAX_SPLIT_PARTS = 1 << 24;   // bound on max_parts (slot indices stay int32)
 constexpr int MAX_NB = 4096;     // key blocks per head supported by the plan
 inline int tlist_cap(const Geo& g) { return 2 * g.nb; }   // union entries per item
+// floats of one partial-result slot: O^T for the item's two query blocks, then
+// the reference maximum (exp2 domain) and the sum of each query
+inline size_t part_floats(const Geo& g) { return (size_t)2 * g.Bt * g.d + 4 * (size_t)g.Bt; }
 
 }  // namespace abs_impl

@@ -118,8 +118,14 @@ def main():
     ap.add_argument("--heads", type=int, default=None,
                     help="run only the first H heads of the workload (one rank's share when "
                          "the layer is sharded by head across GPUs)")
-    ap.add_argument("--sched", default="xcd_local",
-                    choices=["nnz_sorted", "head_major", "head_phased", "xcd_local"])
+    ap.add_argument("--sched", default=None,
+                    choices=["nnz_sorted", "head_major", "head_phased", "xcd_local"],
+                    help="work order (default xcd_local; head_phased with --split)")
+    ap.add_argument("--split", type=int, default=None,
+                    help="split-and-merge attention: cut work items whose union list is longer "
+                         "than SPLIT entries into parts, merge the parts by log-sum-exp")
+    ap.add_argument("--max-parts", type=int, default=None,
+                    help="partial-result slots for --split (default: one per work item)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--timed-only", action="store_true",
                     help="run only the warmup and timed steps (no schedule sweep, cold step or "
@@ -159,6 +165,13 @@ def main():
             sys.exit(2)
         wl = dataclasses.replace(wl, heads=args.heads, name=f"{wl.name}-first{args.heads}heads")
     p = float(np.float32(args.p if args.p is not None else wl.p[0]))
+    split = args.split is not None
+    if args.sched is None:
+        args.sched = "head_phased" if split else "xcd_local"
+    if split and args.sched not in ("nnz_sorted", "head_phased"):
+        print("--split runs on the sorted queues: --sched nnz_sorted or head_phased",
+              file=sys.stderr)
+        sys.exit(2)
     sched = A.SCHEDULES[args.sched]
     print(f"[bench] generating {wl.name}", file=sys.stderr, flush=True)
     inputs = si.make_inputs(wl)
@@ -166,9 +179,27 @@ def main():
     plan = A.plan_init(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.block, wl.dtype)
     mask = A.Mask(plan, dev)
     rws = A.workspace(plan.route_ws_bytes, dev)
-    aws = A.workspace(plan.attend_ws_bytes, dev)
+    max_parts = 0
+    if split:
+        max_parts = args.max_parts if args.max_parts is not None else A.attend_grid(
+            plan, A.SCHED_HEAD_MAJOR)   # the number of work items
+        aws = A.workspace(A.attend_split_ws_bytes(plan, max_parts), dev)
+    else:
+        aws = A.workspace(plan.attend_ws_bytes, dev)
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream()
+
+    def prepare(msk, s_):
+        if split:
+            A.attend_prepare_split(plan, k, v, msk, s_, args.split, max_parts, aws)
+        else:
+            A.attend_prepare(plan, k, v, msk, s_, aws)
+
+    def run(msk, out, s_, telemetry=None):
+        if split:
+            A.attend_run_split(plan, q, msk, out, s_, max_parts, aws, telemetry=telemetry)
+        else:
+            A.attend_run(plan, q, k, msk, out, s_, aws, telemetry=telemetry)
 
     def step(ev=None):
         if ev is not None:
@@ -176,10 +207,10 @@ def main():
         A.route(plan, q, k, p, wl.k_floor, wl.slack, mask=mask, ws=rws)
         if ev is not None:
             ev[1].record(stream)
-        A.attend_prepare(plan, k, v, mask, sched, aws)
+        prepare(mask, sched)
         if ev is not None:
             ev[2].record(stream)
-        A.attend_run(plan, q, k, mask, o, sched, aws)
+        run(mask, o, sched)
         if ev is not None:
             ev[3].record(stream)
 
@@ -218,18 +249,23 @@ def main():
     # head-major hardware dispatch included)
     bal = {}
     o2 = torch.empty_like(q)
-    for name, s in ({} if args.timed_only else A.SCHEDULES).items():
+    sweep = {} if args.timed_only else A.SCHEDULES
+    if split and not args.timed_only:
+        sweep = {n: A.SCHEDULES[n] for n in ("nnz_sorted", "head_phased")}
+    for name, s in sweep.items():
         try:
             n_wg = A.attend_grid(plan, s)
         except A.AbsError:
             continue
         tel = torch.zeros(n_wg * 4, dtype=torch.int64, device=dev)
-        A.attend_prepare(plan, k, v, mask, s, aws)
-        A.attend_run(plan, q, k, mask, o2, s, aws, telemetry=tel)
+        prepare(mask, s)
+        run(mask, o2, s, telemetry=tel)
+        for _ in range(2):       # settle clocks before timing
+            run(mask, o2, s)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(3):
-            A.attend_run(plan, q, k, mask, o2, s, aws)
+            run(mask, o2, s)
         e1.record(stream)
         torch.cuda.synchronize()
         t = tel.cpu().numpy().reshape(-1, 4)
@@ -237,7 +273,7 @@ def main():
         bal[name] = imbalance(t)
         bal[name]["ms_attend_kernel"] = round(e0.elapsed_time(e1) / 3, 4)
         bal[name]["xcds_seen"] = int(len(set((t[:, 1] & 0xF).tolist())))
-    A.attend_prepare(plan, k, v, mask, sched, aws)   # restore the timed schedule
+    prepare(mask, sched)   # restore the timed schedule
 
     # cold step: L2 and Infinity Cache flushed by writing 512 MB first
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -256,18 +292,18 @@ def main():
     if not args.timed_only:
         dmask = A.Mask(plan, dev)
         A.route(plan, q, k, 1.0, 1, 0.0, mask=dmask, ws=rws)
-        A.attend_prepare(plan, k, v, dmask, sched, aws)
-        A.attend_run(plan, q, k, dmask, o2, sched, aws)
+        prepare(dmask, sched)
+        run(dmask, o2, sched)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(2):
-            A.attend_run(plan, q, k, dmask, o2, sched, aws)
+            run(dmask, o2, sched)
         e1.record(stream)
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1) / 2
         dense_tiles = int(dmask.row_ptr[-1].item())
         del dmask
-        A.attend_prepare(plan, k, v, mask, sched, aws)
+        prepare(mask, sched)
         dense = {"ms_attend_kernel": round(dense_ms, 4), "tiles": dense_tiles,
                  "tflops": round(4.0 * bt * bt * d * dense_tiles / (dense_ms * 1e-3) / 1e12, 2),
                  "speedup_sparse_over_dense": round(dense_ms / t_attn, 3)}
@@ -296,6 +332,8 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads,
                    "head_dim": wl.head_dim, "grid": list(wl.grid), "block": list(wl.block),
                    "p": p, "k_floor": wl.k_floor, "slack": wl.slack, "sched": args.sched,
+                   "split": ({"split_tiles": args.split, "max_parts": max_parts} if split
+                             else None),
                    "kept_tiles": nnz, "density": round(nnz / (rp.size - 1) / nb, 4),
                    "head_density_min_median_max": [round(float(dens.min()), 4),
                                                    round(float(np.median(dens)), 4),
@@ -307,8 +345,10 @@ def main():
         "tflops_valid_pairs_layer": round(valid_flops / (ms_step * 1e-3) / 1e12, 2),
         "roofline": {"bound": "mfma", "achieved": round(eff_attn, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(eff_attn / peak, 4),
-                     "traffic": measured_traffic(args.workload, args.sched),
-                     "kernel": ("attn_bf16_kernel<128,128,false>" if args.sched == "head_major"
+                     "traffic": None if split else measured_traffic(args.workload, args.sched),
+                     "kernel": ("attn_bf16_kernel<128,128,true,true> + merge_parts_kernel"
+                                if split else
+                                "attn_bf16_kernel<128,128,false>" if args.sched == "head_major"
                                 else "attn_bf16_kernel<128,128,true>"),
                      "per_unit": "4*Bt^2*d flop per kept tile"},
         "route_hbm": {"bytes_read_qk": 2 * wl.tokens * wl.heads * wl.head_dim * 2,

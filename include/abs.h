@@ -176,6 +176,52 @@ abs_status abs_attend(const abs_plan* plan, const void* q, const void* k, const 
  * the current device (the telemetry record count).  Host query. */
 abs_status abs_attend_grid(const abs_plan* plan, int32_t sched, int32_t* workgroups);
 
+/* Split-and-merge attention (bf16 plans; persistent sorted queues, i.e. sched
+ * ABS_SCHED_NNZ_SORTED or ABS_SCHED_HEAD_PHASED).  Load balancing over compute
+ * units (explainer "Core method" part 2) is limited by the size of the largest
+ * work item; this mode cuts heavy items into parts that run on different
+ * workgroups and combines the parts' partial softmax results by their
+ * log-sum-exp, the merge the APB-V paper notes ("APB-V: Accelerating
+ * Long-Video Understanding via Sequence-Parallelism-aware Approximate
+ * Attention", key design 2) use to join one query block's attention computed
+ * on several hosts.
+ *
+ * A work item (see abs_attend_prepare) walks the ascending union of its two
+ * rows' kept key blocks, nt entries.  With split_tiles = S, an item with
+ * nt > S becomes P = ceil(nt / S) parts, part p taking union entries
+ * [p*nt/P, (p+1)*nt/P) (integer division), provided the running sum of P over
+ * all such items up to and including it, in item order, is at most max_parts;
+ * later heavy items stay whole.  Each part writes float32 partials (O not yet
+ * normalised, its reference maximum and its sum, per query); a merge kernel
+ * then writes o for the cut items.  The result is the same softmax up to
+ * rounding (parts' partials are float32, combined in ascending part order), is
+ * bitwise independent of the queue order, and equals abs_attend_run's output
+ * bitwise for items that are not cut.  The queue is sorted by part length (in
+ * union entries), longest first.
+ *
+ * On return (stream order) from abs_attend_prepare_split the workspace starts
+ * with the work-unit table, int32 [items + max_parts][4]: one entry
+ * {item, t0, t1, slot} per unit (slot -1 for an item that is not cut), units
+ * of an item consecutive, items in ascending order; entries past the last
+ * unit are unspecified.
+ *
+ * Workspace: abs_attend_split_ws_bytes(plan, max_parts) bytes, which holds
+ * max_parts slots of (2*Bt*d + 4*Bt) floats each (133 120 bytes for Bt = 128,
+ * d = 128) on top of the plain attend workspace; a slot count above 2^24 is
+ * rejected (ABS_EINVAL).  The same ws, mask, sched and max_parts go to
+ * abs_attend_prepare_split and then abs_attend_run_split, in stream order.
+ * Telemetry has abs_attend_grid(plan, sched) records, tiles counting the kept
+ * (row, key block) pairs each workgroup processed.  Errors: ABS_EINVAL for
+ * another sched, split_tiles < 1, max_parts outside [0, 2^24] or null
+ * pointers; ABS_ENOTSUP for float32 plans; ABS_ENOSPACE for a small ws. */
+abs_status abs_attend_split_ws_bytes(const abs_plan* plan, int32_t max_parts, size_t* bytes);
+abs_status abs_attend_prepare_split(const abs_plan* plan, const void* k, const void* v,
+                                    const abs_mask* mask, int32_t sched, int32_t split_tiles,
+                                    int32_t max_parts, void* ws, size_t ws_bytes, void* stream);
+abs_status abs_attend_run_split(const abs_plan* plan, const void* q, const abs_mask* mask,
+                                void* o, int32_t sched, int32_t max_parts, void* ws,
+                                size_t ws_bytes, int64_t* telemetry, void* stream);
+
 /* Static description of a status code. */
 const char* abs_status_string(abs_status status);
 

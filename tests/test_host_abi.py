@@ -127,3 +127,55 @@ def test_attend_validation(sched, ws_small, want):
     st = lib.abs_attend(ctypes.byref(plan), None, FAKE, FAKE, ctypes.byref(cm), FAKE, 0, FAKE,
                         plan.attend_ws_bytes, None, None)
     assert st == A.EINVAL
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(), A.OK),
+    (dict(sched=A.SCHED_HEAD_PHASED), A.OK),
+    (dict(sched=A.SCHED_HEAD_MAJOR), A.EINVAL),
+    (dict(sched=A.SCHED_XCD_LOCAL), A.EINVAL),
+    (dict(sched=9), A.EINVAL),
+    (dict(split=0), A.EINVAL),
+    (dict(max_parts=-1), A.EINVAL),
+    (dict(max_parts=(1 << 24) + 1), A.EINVAL),
+    (dict(dtype=A.F32), A.ENOTSUP),
+    (dict(small=True), A.ENOSPACE),
+    (dict(q=None), A.EINVAL),
+])
+def test_attend_split_validation(kw, want):
+    lib = _lib()
+    plan = _plan(kw.get("dtype", A.BF16))
+    sched, split, max_parts = kw.get("sched", 0), kw.get("split", 8), kw.get("max_parts", 16)
+    cm = A.CMask(0x100000, 0x200000, 0x300000)
+    n = ctypes.c_size_t(0)
+    st = lib.abs_attend_split_ws_bytes(ctypes.byref(plan), max_parts, ctypes.byref(n))
+    if want == A.OK or kw.get("small") or "q" in kw or "sched" in kw or "split" in kw:
+        assert st == A.OK
+        need = n.value
+    else:
+        assert st == want
+        need = 1 << 40
+    if want == A.OK:
+        return   # a valid call would launch: the GPU tests cover it
+    nbytes = 1024 if kw.get("small") else need
+    q = kw.get("q", FAKE)
+    if "q" not in kw:   # prepare takes no q
+        st = lib.abs_attend_prepare_split(ctypes.byref(plan), FAKE, FAKE, ctypes.byref(cm), sched,
+                                          split, max_parts, FAKE, nbytes, None)
+        assert st == want
+    if "split" not in kw:   # run takes no split
+        st = lib.abs_attend_run_split(ctypes.byref(plan), q, ctypes.byref(cm), FAKE, sched,
+                                      max_parts, FAKE, nbytes, None, None)
+        assert st == want
+
+
+def test_attend_split_workspace_size():
+    _lib()
+    plan = _plan()
+    base = A.attend_split_ws_bytes(plan, 0)
+    assert base >= plan.attend_ws_bytes
+    slot = (2 * plan.block_tokens * plan.s.head_dim + 4 * plan.block_tokens) * 4
+    more = A.attend_split_ws_bytes(plan, 100)
+    assert more - base >= 100 * slot
+    lib = _lib()
+    assert lib.abs_attend_split_ws_bytes(ctypes.byref(plan), 4, None) == A.EINVAL
