@@ -389,35 +389,44 @@ def schedule(costs, mode: str, items_per_head: Optional[int] = None,
 def split_units(union_counts, split: int, max_parts: int):
     """Cut heavy work items into parts for the split-and-merge attention.
 
-    Source: FVAttn explainer, part 2 (balance the work handed to each worker;
-    a single heavy head bounds how even that can be) and the APB-V paper notes
-    ("APB-V: Accelerating Long-Video Understanding via Sequence-Parallelism-aware
-    Approximate Attention"), key design 2: one query block's attention computed
-    in pieces on several hosts is joined through FlashAttention's log-sum-exp.
-    Reading on one GPU: a work item walks the ascending union of its rows' kept
-    key blocks (union_counts[i] entries); an item with nt > split entries
-    becomes P = ceil(nt / split) parts, part q taking entries
-    [q nt // P, (q + 1) nt // P); items are cut in item order while the running
-    sum of P over every such item so far (cut or not) stays within max_parts,
-    and each part owns the next result slot.
+    Source: FVAttn explainer, part 2 (balance the work handed to each worker by
+    acting on the heaviest units first: the top-k heavy heads are the ones
+    moved) and the APB-V paper notes ("APB-V: Accelerating Long-Video
+    Understanding via Sequence-Parallelism-aware Approximate Attention"), key
+    design 2: one query block's attention computed in pieces on several hosts
+    is joined through FlashAttention's log-sum-exp.  Reading on one GPU: a work
+    item walks the ascending union of its rows' kept key blocks
+    (union_counts[i] entries); an item with nt > split entries wants
+    P = ceil(nt / split) parts, part q taking entries [q nt // P, (q+1) nt // P).
+    Items are cut heaviest first (nt descending, ties by item index) while the
+    running sum of their P stays within max_parts; the first that does not fit
+    ends the cutting.  Result slots are numbered over the cut items in item
+    order, consecutively within an item.
 
     Returns (units, cut): units = [(item, t0, t1, slot)] in item order, slot -1
-    for an item left whole; cut = [(item, first_slot, P)].
+    for an item left whole; cut = [(item, first_slot, P)] in item order.
     """
+    counts = [int(x) for x in union_counts]
+    parts = [-(-nt // split) if nt > split else 1 for nt in counts]
+    heavy = sorted((i for i, nt in enumerate(counts) if nt > split),
+                   key=lambda i: (-counts[i], i))
+    chosen, used = set(), 0
+    for i in heavy:
+        if used + parts[i] > max_parts:
+            break
+        chosen.add(i)
+        used += parts[i]
     units, cut = [], []
-    wanted = 0
     slot = 0
-    for item, nt in enumerate(int(x) for x in union_counts):
-        parts = -(-nt // split) if nt > split else 1
-        if parts > 1:
-            wanted += parts
-            if wanted <= max_parts:
-                cut.append((item, slot, parts))
-                for q in range(parts):
-                    units.append((item, q * nt // parts, (q + 1) * nt // parts, slot + q))
-                slot += parts
-                continue
-        units.append((item, 0, nt, -1))
+    for item, nt in enumerate(counts):
+        if item in chosen:
+            P = parts[item]
+            cut.append((item, slot, P))
+            for q in range(P):
+                units.append((item, q * nt // P, (q + 1) * nt // P, slot + q))
+            slot += P
+        else:
+            units.append((item, 0, nt, -1))
     return units, cut
 
 

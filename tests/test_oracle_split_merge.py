@@ -33,7 +33,7 @@ def test_split_units_golden():
             assert got_u == _triples(units, 4), line
             assert got_c == _triples(cut, 3), line
             n += 1
-    assert n == 6
+    assert n == 8
 
 
 @pytest.mark.parametrize("seed", range(8))
@@ -61,12 +61,14 @@ def test_split_units_invariants(seed):
             cut_items.append(item)
         else:
             assert parts[0][2] == -1
-    # slots: consecutive from 0, within the budget; cut items form a prefix of
-    # the items that want cutting
+    # slots: consecutive from 0, within the budget; the cut items are the
+    # heaviest of those that want cutting (nt descending, ties by index), and
+    # the next of them would not have fitted
     slots = [s for _, _, _, s in units if s >= 0]
     assert slots == list(range(len(slots))) and len(slots) <= max_parts
-    wanting = [i for i, nt in enumerate(counts) if nt > split]
-    assert cut_items == wanting[:len(cut_items)]
+    wanting = sorted((i for i, nt in enumerate(counts) if nt > split),
+                     key=lambda i: (-counts[i], i))
+    assert sorted(cut_items) == sorted(wanting[:len(cut_items)])
     if len(cut_items) < len(wanting):
         nxt = wanting[len(cut_items)]
         assert len(slots) + math.ceil(counts[nxt] / split) > max_parts
