@@ -349,15 +349,20 @@ __global__ __launch_bounds__(256) void tile_list_kernel(Geo g, const int* __rest
 
 // ---------------------------------------------------------------------------
 // Split-and-merge queue (one workgroup).  A work item whose union list holds
-// nt > split entries is cut into P = ceil(nt / split) parts, part p covering
-// entries [p nt / P, (p+1) nt / P) (integer division, every part non-empty),
-// as long as the running total of parts over all such items up to and
-// including it, in item order, stays within max_parts (that total only grows,
-// so the items cut are a prefix of the heavy ones).  Each part owns one partial-result slot; an
+// nt > split entries wants P = ceil(nt / split) parts, part q covering entries
+// [q nt / P, (q+1) nt / P) (integer division, every part non-empty).  Items
+// are cut heaviest first (nt descending, ties by item index) while the running
+// sum of their P stays within max_parts; the first item that does not fit ends
+// the cutting.  Found without sorting: with w(v) = (items with nt == v) x P(v)
+// and the suffix sums S(v) = sum over u >= v of w(u), the cut is every item
+// with nt > tau plus the first floor((max_parts - S(tau+1)) / P(tau)) items
+// (in item order) with nt == tau, where tau is the largest v with
+// S(v) > max_parts (no tau: every heavy item is cut).  Each part owns one
+// partial-result slot (slots numbered over the cut items in item order); an
 // item that is not cut is one unit that writes its output directly.
 //   units[u] = {item, t0, t1, slot or -1}, units of an item consecutive, items
 //              in order;
-//   stab[s]  = {item, first slot, P, 0} for the s-th item that is cut;
+//   stab[s]  = {item, first slot, P, 0} for the s-th cut item (item order);
 //   counter[NUNITS], counter[NSPLIT] = number of units, of cut items.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void split_units_kernel(Geo g, const int* __restrict__ tcount,
@@ -365,20 +370,52 @@ __global__ __launch_bounds__(1024) void split_units_kernel(Geo g, const int* __r
                                                            int4* __restrict__ units,
                                                            int4* __restrict__ stab,
                                                            int* __restrict__ counter) {
-  constexpr int NT = 1024;
+  constexpr int NT = 1024, VPT = (2 * MAX_NB + 1 + NT - 1) / NT;   // values per thread
+  __shared__ int cnt[2 * MAX_NB + 1];
   __shared__ int tmp[NT / 64 + 1];
-  int want_base = 0, slot_base = 0, unit_base = 0, split_base = 0;
+  __shared__ int s_tau, s_allow;
+  const int nv = 2 * g.nb + 1;   // union counts 0 .. 2nb
+  auto parts_of = [&](int nt) { return nt > split ? (nt + split - 1) / split : 1; };
+  for (int v = threadIdx.x; v < nv; v += NT) cnt[v] = 0;
+  if (threadIdx.x == 0) { s_tau = -1; s_allow = 0; }
+  __syncthreads();
+  for (int i = threadIdx.x; i < g.groups; i += NT) {
+    const int nt = tcount[i];
+    if (nt > split) atomicAdd(&cnt[nt], 1);
+  }
+  __syncthreads();
+  // suffix sums over values, high to low: thread t owns reversed positions
+  // r = VPT t .. VPT t + VPT - 1, value v = nv - 1 - r
+  int wv[VPT], loc = 0;
+#pragma unroll
+  for (int e = 0; e < VPT; ++e) {
+    const int v = nv - 1 - (VPT * (int)threadIdx.x + e);
+    wv[e] = (v > split && v >= 0) ? cnt[v] * parts_of(v) : 0;
+    loc += wv[e];
+  }
+  int total;
+  int run = block_exclusive_scan<NT>(loc, tmp, &total);   // S(v) of values above this chunk
+#pragma unroll
+  for (int e = 0; e < VPT; ++e) {
+    const int v = nv - 1 - (VPT * (int)threadIdx.x + e);
+    const int above = run;           // S(v + 1)
+    run += wv[e];                    // S(v)
+    if (v > split && run > max_parts && above <= max_parts) {
+      s_tau = v;
+      s_allow = (max_parts - above) / parts_of(v);
+    }
+  }
+  __syncthreads();
+  const int tau = s_tau, allow = s_allow;
+  int slot_base = 0, unit_base = 0, split_base = 0, eq_base = 0;
   for (int i0 = 0; i0 < g.groups; i0 += NT) {
     const int i = i0 + threadIdx.x;
-    int nt = 0, P = 1;
-    if (i < g.groups) {
-      nt = tcount[i];
-      P = nt > split ? (nt + split - 1) / split : 1;
-    }
-    const int want = P > 1 ? P : 0;
-    int tot;
-    const int wpre = block_exclusive_scan<NT>(want, tmp, &tot);
-    const bool cut = want > 0 && want_base + wpre + want <= max_parts;
+    const int nt = i < g.groups ? tcount[i] : 0;
+    const int P = parts_of(nt);
+    const bool at_tau = i < g.groups && nt > split && nt == tau;
+    int eq_tot;
+    const int eq_rank = eq_base + block_exclusive_scan<NT>(at_tau ? 1 : 0, tmp, &eq_tot);
+    const bool cut = i < g.groups && nt > split && (nt > tau || (at_tau && eq_rank < allow));
     const int nu = i < g.groups ? (cut ? P : 1) : 0;
     int utot, stot, ctot;
     const int upre = block_exclusive_scan<NT>(nu, tmp, &utot);
@@ -394,7 +431,7 @@ __global__ __launch_bounds__(1024) void split_units_kernel(Geo g, const int* __r
         units[u0] = make_int4(i, 0, nt, -1);
       }
     }
-    want_base += tot;
+    eq_base += eq_tot;
     slot_base += ctot;
     unit_base += utot;
     split_base += stot;
@@ -820,67 +857,70 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the parts of every cut work item (one workgroup per cut item).
-// Part p left, per query, O_p = sum over its keys of 2^(c s - m_p) v, its sum
-// l_p and its reference m_p (exp2 domain, -inf when the part had no key of the
-// query's row).  With M = max_p m_p and weights w_p = 2^(m_p - M), the
-// softmax over the union of the parts' keys is
+// Merge of the parts of every cut work item.  Part p left, per query,
+// O_p = sum over its keys of 2^(c s - m_p) v, its sum l_p and its reference
+// m_p (exp2 domain, -inf when the part had no key of the query's row).  With
+// M = max_p m_p and weights w_p = 2^(m_p - M), the softmax over the union of
+// the parts' keys is
 //   O = (sum_p w_p O_p) / (sum_p w_p l_p),
 // the same log-sum-exp combination as merging attention computed over
 // disjoint key sets.  Parts are combined in ascending order, so the result does
-// not depend on the schedule.  Thread f handles 4 consecutive d of one query.
+// not depend on the schedule.  Workgroup x = (cut item, chunk of 256 float4
+// columns of the item's 2 Bt x d output); one thread per 4 consecutive d of one
+// query, so every load of a workgroup is in flight at once.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void merge_parts_kernel(Geo g, const int* __restrict__ stab,
                                                           const int* __restrict__ counter,
                                                           const float* __restrict__ part,
-                                                          long pf, bf16_t* __restrict__ o) {
-  const int sidx = blockIdx.x;
+                                                          long pf, int chunks,
+                                                          bf16_t* __restrict__ o) {
+  const int sidx = blockIdx.x / chunks, chunk = blockIdx.x % chunks;
   if (sidx >= counter[NSPLIT]) return;
+  const int BT = g.Bt, D = g.d, C4 = D / 4;
+  const int f = chunk * 256 + threadIdx.x;
+  if (f >= 2 * BT * C4) return;
   const int item = stab[4 * sidx], slot0 = stab[4 * sidx + 1], P = stab[4 * sidx + 2];
   const int bhh = item / g.groups_per_head, gl = item % g.groups_per_head;
   int lead, partner;
   group_blocks(g, gl, &lead, &partner);
+  const int qi = f / C4, c4 = f % C4;
+  const int half = qi / BT, qs = qi % BT;
+  const int blk = half ? partner : lead;
+  if (blk < 0) return;
+  const int plane = g.bh * g.bw;
+  const int tb = blk / (g.nbh * g.nbw), hb = (blk / g.nbw) % g.nbh, wb = blk % g.nbw;
+  const int tt = tb * g.bt + qs / plane, hh = hb * g.bh + (qs / g.bw) % g.bh,
+            ww = wb * g.bw + qs % g.bw;
+  if (tt >= g.T || hh >= g.Hg || ww >= g.W) return;   // padding slot: no output
+  const long n = ((long)tt * g.Hg + hh) * g.W + ww;
   const int b = bhh / g.H, h = bhh % g.H;
-  const int BT = g.Bt, D = g.d, C4 = D / 4;
   const float* base = part + (long)slot0 * pf;
   const long mo = 2l * BT * D, lo = mo + 2 * BT;
-  const int plane = g.bh * g.bw;
-  for (int f = threadIdx.x; f < 2 * BT * C4; f += blockDim.x) {
-    const int qi = f / C4, c4 = f % C4;
-    const int half = qi / BT, qs = qi % BT;
-    const int blk = half ? partner : lead;
-    if (blk < 0) continue;
-    const int tb = blk / (g.nbh * g.nbw), hb = (blk / g.nbw) % g.nbh, wb = blk % g.nbw;
-    const int tt = tb * g.bt + qs / plane, hh = hb * g.bh + (qs / g.bw) % g.bh,
-              ww = wb * g.bw + qs % g.bw;
-    if (tt >= g.T || hh >= g.Hg || ww >= g.W) continue;   // padding slot: no output
-    const long n = ((long)tt * g.Hg + hh) * g.W + ww;
-    float M = -INFINITY;
-    for (int p = 0; p < P; ++p) M = fmaxf(M, base[p * pf + mo + qi]);
-    float L = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (M > -INFINITY) {
-      for (int p = 0; p < P; ++p) {
-        const float* sp = base + p * pf;
-        const float wgt = __builtin_amdgcn_exp2f(sp[mo + qi] - M);
-        L = fmaf(wgt, sp[lo + qi], L);
-        const float4 v = *reinterpret_cast<const float4*>(sp + (long)qi * D + 4 * c4);
-        acc.x = fmaf(wgt, v.x, acc.x);
-        acc.y = fmaf(wgt, v.y, acc.y);
-        acc.z = fmaf(wgt, v.z, acc.z);
-        acc.w = fmaf(wgt, v.w, acc.w);
-      }
+  float M = -INFINITY;
+  for (int p = 0; p < P; ++p) M = fmaxf(M, base[p * pf + mo + qi]);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (M > -INFINITY) {
+    for (int p = 0; p < P; ++p) {
+      const float* sp = base + p * pf;
+      const float wgt = __builtin_amdgcn_exp2f(sp[mo + qi] - M);
+      L = fmaf(wgt, sp[lo + qi], L);
+      const float4 v = *reinterpret_cast<const float4*>(sp + (long)qi * D + 4 * c4);
+      acc.x = fmaf(wgt, v.x, acc.x);
+      acc.y = fmaf(wgt, v.y, acc.y);
+      acc.z = fmaf(wgt, v.z, acc.z);
+      acc.w = fmaf(wgt, v.w, acc.w);
     }
-    const float inv = L > 0.f ? 1.0f / L : 0.f;
-    const __bf16 v0 = (__bf16)(acc.x * inv), v1 = (__bf16)(acc.y * inv);
-    const __bf16 v2 = (__bf16)(acc.z * inv), v3 = (__bf16)(acc.w * inv);
-    const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
-    const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, v2) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
-    *reinterpret_cast<uint2*>(o + (((long)b * g.N + n) * g.H + h) * D + 4 * c4) =
-        make_uint2(w0, w1);
   }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  const __bf16 v0 = (__bf16)(acc.x * inv), v1 = (__bf16)(acc.y * inv);
+  const __bf16 v2 = (__bf16)(acc.z * inv), v3 = (__bf16)(acc.w * inv);
+  const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
+  const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, v2) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
+  *reinterpret_cast<uint2*>(o + (((long)b * g.N + n) * g.H + h) * D + 4 * c4) =
+      make_uint2(w0, w1);
 }
 
 // ---------------------------------------------------------------------------
@@ -1173,10 +1213,11 @@ hipError_t launch_attend_run_split(const Geo& g, const void* q, const abs_mask* 
   }
   // every cut item has at least two parts
   const long most = (long)max_parts / 2 < (long)g.groups ? (long)max_parts / 2 : (long)g.groups;
+  const int chunks = (2 * g.Bt * (g.d / 4) + 255) / 256;
   if (most > 0)
-    hipLaunchKernelGGL(merge_parts_kernel, dim3((unsigned)most), dim3(256), 0, s, g,
+    hipLaunchKernelGGL(merge_parts_kernel, dim3((unsigned)(most * chunks)), dim3(256), 0, s, g,
                        (const int*)(ws + L.stab), (const int*)(ws + L.counter),
-                       (const float*)(ws + L.part), (long)part_floats(g), (bf16_t*)o);
+                       (const float*)(ws + L.part), (long)part_floats(g), chunks, (bf16_t*)o);
   return hipGetLastError();
 }
 

@@ -125,7 +125,8 @@ def main():
                     help="split-and-merge attention: cut work items whose union list is longer "
                          "than SPLIT entries into parts, merge the parts by log-sum-exp")
     ap.add_argument("--max-parts", type=int, default=None,
-                    help="partial-result slots for --split (default: one per work item)")
+                    help="partial-result slots for --split (default: two per persistent "
+                         "workgroup)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--timed-only", action="store_true",
                     help="run only the warmup and timed steps (no schedule sweep, cold step or "
@@ -181,8 +182,9 @@ def main():
     rws = A.workspace(plan.route_ws_bytes, dev)
     max_parts = 0
     if split:
-        max_parts = args.max_parts if args.max_parts is not None else A.attend_grid(
-            plan, A.SCHED_HEAD_MAJOR)   # the number of work items
+        # default: two slots per persistent workgroup (the heaviest items are cut first)
+        max_parts = (args.max_parts if args.max_parts is not None
+                     else 2 * A.attend_grid(plan, sched))
         aws = A.workspace(A.attend_split_ws_bytes(plan, max_parts), dev)
     else:
         aws = A.workspace(plan.attend_ws_bytes, dev)
@@ -348,8 +350,9 @@ def main():
                      "traffic": None if split else measured_traffic(args.workload, args.sched),
                      "kernel": ("attn_bf16_kernel<128,128,true,true> + merge_parts_kernel"
                                 if split else
-                                "attn_bf16_kernel<128,128,false>" if args.sched == "head_major"
-                                else "attn_bf16_kernel<128,128,true>"),
+                                "attn_bf16_kernel<128,128,false,false>"
+                                if args.sched == "head_major"
+                                else "attn_bf16_kernel<128,128,true,false>"),
                      "per_unit": "4*Bt^2*d flop per kept tile"},
         "route_hbm": {"bytes_read_qk": 2 * wl.tokens * wl.heads * wl.head_dim * 2,
                       "gbs_algorithmic": round(2 * wl.tokens * wl.heads * wl.head_dim * 2

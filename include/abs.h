@@ -188,10 +188,11 @@ abs_status abs_attend_grid(const abs_plan* plan, int32_t sched, int32_t* workgro
  *
  * A work item (see abs_attend_prepare) walks the ascending union of its two
  * rows' kept key blocks, nt entries.  With split_tiles = S, an item with
- * nt > S becomes P = ceil(nt / S) parts, part p taking union entries
- * [p*nt/P, (p+1)*nt/P) (integer division), provided the running sum of P over
- * all such items up to and including it, in item order, is at most max_parts;
- * later heavy items stay whole.  Each part writes float32 partials (O not yet
+ * nt > S wants P = ceil(nt / S) parts, part p taking union entries
+ * [p*nt/P, (p+1)*nt/P) (integer division).  Items are cut heaviest first (nt
+ * descending, ties by lower item index) while the running sum of their P stays
+ * within max_parts; the first that does not fit ends the cutting, and the rest
+ * stay whole.  Slots are numbered over the cut items in item order.  Each part writes float32 partials (O not yet
  * normalised, its reference maximum and its sum, per query); a merge kernel
  * then writes o for the cut items.  The result is the same softmax up to
  * rounding (parts' partials are float32, combined in ascending part order), is

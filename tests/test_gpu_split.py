@@ -126,13 +126,16 @@ def test_split_everything_small(name, split):
     assert np.array_equal(o, o2)
 
 
-def test_split_budget_cuts_a_prefix():
+def test_split_budget_cuts_the_heaviest():
     c = Case(SMALL["d128-bt128-ragged"])
     split = 2
     full = _wanted(c.counts, split)
     max_parts = full // 3
-    o, units, cut = c.run_split(split, max_parts)
+    o, units, cut = c.run_split(split, max_parts)   # unit table checked against the oracle
     assert 0 < len(cut) < sum(1 for n in c.counts if n > split)
+    lightest_cut = min(c.counts[it] for it, _, _ in cut)
+    assert all(c.counts[it] <= lightest_cut for it in range(len(c.counts))
+               if it not in {x[0] for x in cut})
     o_ref = O.sparse_attention(*(t.float().numpy() for t in c.inputs), c.geo, c.rp, c.ci)
     compare_outputs(o, o_ref, c.geo, range(c.bh * c.geo.nb), c.wl.heads, "bf16")
     c.check_rows_equal(o, c.o_plain.float().cpu().numpy(), c.whole_rows(cut))
@@ -169,16 +172,24 @@ def test_dense_mask_split():
 @pytest.mark.slow
 def test_split_full_480p():
     """The 480p layer (40 heads, 32 760 tokens, p = 0.9) with parts of at most
-    64 union entries and one slot per item on average, in the launch
-    configuration the benchmark times: unit table exact, sampled rows against
-    the oracle, whole items bitwise equal to the plain path."""
+    64 union entries and one slot per item on average, then parts of at most
+    96 entries and 256 slots, in the launch configuration the benchmark times:
+    unit tables exact, sampled rows against the oracle, whole items bitwise
+    equal to the plain path."""
     wl = si.WORKLOADS[1]
     c = Case(wl)
     o, units, cut = c.run_split(64, len(c.groups))
     assert len(cut) > 0
+    # a budget of 256 slots: only the heaviest items are cut
+    o2, _, cut2 = c.run_split(96, 256)
+    assert 0 < len(cut2) < len(cut)
+    whole2 = set(c.whole_rows(cut2))
     q, k, v = (t.float().numpy() for t in c.inputs)
     rows = sample_rows(c.rp, wl.batch, wl.heads, c.geo.nb, c.geo, seed=1)
     o_ref = O.sparse_attention(q, k, v, c.geo, c.rp, c.ci, rows=rows)
     print("max/mean err", compare_outputs(o, o_ref, c.geo, rows, wl.heads, "bf16"))
+    print("max/mean err, 256 slots", compare_outputs(o2, o_ref, c.geo, rows, wl.heads, "bf16"))
     whole = set(c.whole_rows(cut))
-    c.check_rows_equal(o, c.o_plain.float().cpu().numpy(), [r for r in rows if r in whole])
+    plain = c.o_plain.float().cpu().numpy()
+    c.check_rows_equal(o, plain, [r for r in rows if r in whole])
+    c.check_rows_equal(o2, plain, [r for r in rows if r in whole2])
