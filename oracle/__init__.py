@@ -19,6 +19,8 @@ from .abs_oracle import (  # noqa: F401
     select_row,
     route,
     slack_fill,
+    dynamic_slack_fill,
+    slack_budget,
     keep_to_csr,
     csr_to_keep,
     sparse_attention,

@@ -251,6 +251,59 @@ def slack_fill(P: np.ndarray, keep: np.ndarray, slack: float):
     return out, info
 
 
+def dynamic_slack_fill(P: np.ndarray, keep: np.ndarray, budget: int, theta: float):
+    """Add up to `budget` unkept block pairs over the whole batch, highest P first.
+
+    Source: FVAttn explainer, part 3 (capacity that non-critical workers leave
+    idle is filled with high-scoring blocks) and "Lessons for engineering"
+    item 5 (keep only blocks above a score threshold for the fill; the amount
+    injected is the knob to turn down).  Reading on one GPU: the candidates are
+    the unkept pairs (b, h, i, j) with P >= theta, over all heads at once (the
+    compute units are shared by every head); they are ranked by P descending,
+    ties by the lowest linear index ((b*H + h)*nb + i)*nb + j, and the first
+    min(budget, number of candidates) are added.
+    Returns (new_keep, info): info = dict(added, candidates, last, next), the
+    P of the last candidate added and of the first one left out.
+    """
+    B, H, nb, _ = P.shape
+    flat_keep = keep.reshape(-1).copy()
+    flat_p = np.asarray(P, dtype=np.float64).reshape(-1)
+    cand = np.nonzero(~flat_keep & (flat_p >= theta))[0]      # ascending linear index
+    order = np.argsort(-flat_p[cand], kind="stable")
+    n = min(max(int(budget), 0), cand.size)
+    take = cand[order[:n]]
+    flat_keep[take] = True
+    info = dict(added=int(n), candidates=int(cand.size),
+                last=float(flat_p[take[-1]]) if n > 0 else np.nan,
+                next=float(flat_p[cand[order[n]]]) if n < cand.size else np.nan)
+    return flat_keep.reshape(B, H, nb, nb), info
+
+
+def slack_budget(records, fill: float, max_pairs: int) -> int:
+    """Pair budget of the dynamic slack fill, from the telemetry of one
+    persistent attention launch: records [n, 4] = (hardware id, XCC id, kept
+    tiles, busy clock ticks) per workgroup.
+
+    Source: FVAttn explainer, part 3 (after balancing, non-critical workers
+    still go idle before the critical path; that slack is filled) and "Lessons
+    for engineering" item 1 (watch the tail per worker).  Reading on one GPU:
+    the workers are the persistent workgroups; the launch lasts T = max busy;
+    the idle capacity is sum_w (T - busy_w) ticks, worth
+    idle * sum(tiles) / sum(busy) tiles at the launch's mean cost per tile; the
+    budget is floor(fill * that) (the product taken exactly in integers, then
+    one float64 multiply and one divide), clamped to [0, max_pairs].
+    """
+    rec = np.asarray(records, dtype=np.int64).reshape(-1, 4)
+    busy = [int(x) for x in rec[:, 3]]
+    tiles = int(sum(int(x) for x in rec[:, 2]))
+    total = sum(busy)
+    if total <= 0 or tiles <= 0:
+        return 0
+    idle_tiles = (len(busy) * max(busy) - total) * tiles      # exact integer
+    val = math.floor(float(fill) * float(idle_tiles) / float(total))
+    return max(0, min(int(max_pairs), val))
+
+
 def keep_to_csr(keep: np.ndarray):
     """CSR of a [B, H, nb, nb] boolean mask: rows (b, h, i) in order, columns
     ascending.  Returns (row_ptr int64 [rows+1], col_idx int64, head_nnz)."""
