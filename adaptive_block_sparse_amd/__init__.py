@@ -29,7 +29,8 @@ SCHEDULES = {"nnz_sorted": SCHED_NNZ_SORTED, "head_major": SCHED_HEAD_MAJOR,
              "head_phased": SCHED_HEAD_PHASED, "xcd_local": SCHED_XCD_LOCAL}
 EXPORTS = ("abs_plan_init", "abs_route", "abs_attend_prepare", "abs_attend_run",
            "abs_attend", "abs_attend_grid", "abs_status_string", "abs_attend_split_ws_bytes",
-           "abs_attend_prepare_split", "abs_attend_run_split")
+           "abs_attend_prepare_split", "abs_attend_run_split", "abs_route_dynamic",
+           "abs_slack_budget")
 
 
 class Shape(ctypes.Structure):
@@ -82,6 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "abs_attend_split_ws_bytes": [P, I32, ctypes.POINTER(SZ)],
         "abs_attend_prepare_split": [P, V, V, M, I32, I32, I32, V, SZ, V],
         "abs_attend_run_split": [P, V, M, V, I32, I32, V, SZ, V, V],
+        "abs_route_dynamic": [P, V, V, F, I32, F, V, M, V, SZ, V],
+        "abs_slack_budget": [P, I32, V, F, ctypes.c_int64, V, V],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -182,6 +185,31 @@ def route(plan: Plan, q, k, p: float, k_floor: int, slack: float = 0.0,
                                   _stream(stream))
     _check("abs_route", st)
     return mask
+
+
+def route_dynamic(plan: Plan, q, k, p: float, k_floor: int, theta: float, budget,
+                  mask: Optional[Mask] = None, ws=None, stream=None) -> Mask:
+    """Routing plus a dynamic slack fill of up to budget[0] pairs (a device
+    int64 tensor), candidates P >= theta over the whole batch, highest P first."""
+    _check_qkv(plan, q, k)
+    mask = Mask(plan, q.device) if mask is None else mask
+    ws = workspace(plan.route_ws_bytes, q.device) if ws is None else ws
+    cm = mask.c()
+    st = load_library().abs_route_dynamic(ctypes.byref(plan), _ptr(q), _ptr(k), float(p),
+                                          int(k_floor), float(theta), _ptr(budget),
+                                          ctypes.byref(cm), _ptr(ws), ws.numel(), _stream(stream))
+    _check("abs_route_dynamic", st)
+    return mask
+
+
+def slack_budget(plan: Plan, sched: int, telemetry, fill: float, max_pairs: int, budget,
+                 stream=None) -> None:
+    """Write into budget[0] (device int64) the dynamic slack budget derived
+    from one persistent launch's telemetry."""
+    _check("abs_slack_budget",
+           load_library().abs_slack_budget(ctypes.byref(plan), int(sched), _ptr(telemetry),
+                                           float(fill), int(max_pairs), _ptr(budget),
+                                           _stream(stream)))
 
 
 def attend_grid(plan: Plan, sched: int = SCHED_NNZ_SORTED) -> int:

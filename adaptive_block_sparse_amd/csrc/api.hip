@@ -183,6 +183,39 @@ abs_status abs_route(const abs_plan* plan, const void* q, const void* k, float p
   return e == hipSuccess ? ABS_OK : ABS_EHIP;
 }
 
+abs_status abs_route_dynamic(const abs_plan* plan, const void* q, const void* k, float p,
+                             int32_t k_floor, float theta, const int64_t* budget,
+                             const abs_mask* mask, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan_ok(plan) || !q || !k || !budget || !mask_ok(mask) || !ws) return ABS_EINVAL;
+  if (!(p > 0.0f && p <= 1.0f)) return ABS_EINVAL;
+  if (k_floor < 1) return ABS_EINVAL;
+  if (!(theta >= 0.0f && theta <= 1.0f)) return ABS_EINVAL;
+  Geo g = make_geo(plan);
+  RouteWs L = route_ws_layout(g, true);
+  if (ws_bytes < L.total) return ABS_ENOSPACE;
+  const int kf = k_floor > g.nb ? g.nb : k_floor;
+  hipError_t e = launch_route_dynamic(g, plan->s.dtype, q, k, p, kf, theta,
+                                      (const long long*)budget, mask, (char*)ws, L,
+                                      (hipStream_t)stream);
+  return e == hipSuccess ? ABS_OK : ABS_EHIP;
+}
+
+abs_status abs_slack_budget(const abs_plan* plan, int32_t sched, const int64_t* telemetry,
+                            float fill, int64_t max_pairs, int64_t* budget, void* stream) {
+  if (!plan_ok(plan) || !telemetry || !budget) return ABS_EINVAL;
+  if (sched != ABS_SCHED_NNZ_SORTED && sched != ABS_SCHED_HEAD_PHASED &&
+      sched != ABS_SCHED_XCD_LOCAL)
+    return ABS_EINVAL;   // the records must come from a persistent launch
+  if (!(fill >= 0.0f && fill <= 1.0f) || max_pairs < 0) return ABS_EINVAL;
+  if (plan->s.dtype != ABS_BF16) return ABS_ENOTSUP;
+  Geo g = make_geo(plan);
+  const int n = attend_grid(g, plan->s.dtype, sched);
+  if (n <= 0) return ABS_EHIP;
+  hipError_t e = launch_slack_budget((const long long*)telemetry, n, fill, (long long)max_pairs,
+                                     (long long*)budget, (hipStream_t)stream);
+  return e == hipSuccess ? ABS_OK : ABS_EHIP;
+}
+
 abs_status abs_attend_prepare(const abs_plan* plan, const void* k, const void* v,
                               const abs_mask* mask, int32_t sched, void* ws, size_t ws_bytes,
                               void* stream) {

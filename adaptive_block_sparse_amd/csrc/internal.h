@@ -84,6 +84,11 @@ AttendWs attend_ws_layout(const Geo& g, int dtype, int max_parts = -1);
 hipError_t launch_route(const Geo& g, int dtype, const void* q, const void* k, float p,
                         int k_floor, float slack, const abs_mask* mask, char* ws,
                         const RouteWs& L, hipStream_t s);
+hipError_t launch_route_dynamic(const Geo& g, int dtype, const void* q, const void* k, float p,
+                                int k_floor, float theta, const long long* budget,
+                                const abs_mask* mask, char* ws, const RouteWs& L, hipStream_t s);
+hipError_t launch_slack_budget(const long long* telem, int n, float fill, long long max_pairs,
+                               long long* budget, hipStream_t s);
 hipError_t launch_attend_prepare(const Geo& g, int dtype, const void* k, const void* v,
                                  const abs_mask* mask,
                                  int sched, int heads_per_phase, char* ws, const AttendWs& L,

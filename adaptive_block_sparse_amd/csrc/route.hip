@@ -232,11 +232,13 @@ __global__ __launch_bounds__(256) void select_kernel(Geo g, float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Slack fill: per head, add the unkept pairs with the largest P (ties: lowest
-// linear index) until the head holds `budget` pairs.  Exact selection by a
-// three-pass radix select on the float bits of P (non-negative floats order
-// like their bit patterns): 11 + 11 + 10 bits.
-// sel[h] = {need (remaining), prefix, active, need_total}
+// Slack fill over groups of gr consecutive rows: in each group, add the `need`
+// unkept pairs with the largest P among those with P >= theta (ties: lowest
+// linear index).  Exact selection by a three-pass radix select on the float
+// bits of P (non-negative floats order like their bit patterns): 11 + 11 + 10
+// bits.  Groups are heads (fixed per-head budget, gr = nb, theta = 0) or the
+// whole batch (dynamic fill, gr = rows).
+// sel[group] = {need (remaining), prefix, active, need_total}
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void slack_init_kernel(Geo g, const int* __restrict__ count,
                                                          int* __restrict__ sel,
@@ -260,19 +262,35 @@ __global__ __launch_bounds__(256) void slack_init_kernel(Geo g, const int* __res
   }
 }
 
+// Dynamic fill, one group (the whole batch): need = the device-side budget.
+__global__ __launch_bounds__(256) void dslack_init_kernel(int* __restrict__ sel,
+                                                          uint32_t* __restrict__ hist,
+                                                          const long long* __restrict__ budget) {
+  for (int x = threadIdx.x; x < 2048; x += 256) hist[x] = 0u;
+  if (threadIdx.x == 0) {
+    long long need = *budget;
+    need = need < 0 ? 0 : (need > 0x7fffffffll ? 0x7fffffffll : need);
+    sel[0] = (int)need;
+    sel[1] = 0;
+    sel[2] = need > 0 ? 1 : 0;
+    sel[3] = (int)need;
+  }
+}
+
 // shift/width of the digit examined in each pass; prefix holds the bits above
 __device__ __forceinline__ void slack_digit(int pass, int* shift, int* width) {
   *shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
   *width = pass == 2 ? 10 : 11;
 }
 
-// Rows-per-workgroup chunks of one head; histogram of the current digit over
-// unkept pairs whose higher bits equal the prefix chosen so far.
+// Rows-per-workgroup chunks of one group; histogram of the current digit over
+// candidate pairs (unkept, P >= theta) whose higher bits equal the prefix
+// chosen so far.
 __global__ __launch_bounds__(256) void slack_hist_kernel(Geo g, const float* __restrict__ prob,
                                                          const uint32_t* __restrict__ bitmap,
                                                          const int* __restrict__ sel,
                                                          uint32_t* __restrict__ hist, int pass,
-                                                         int rows_per_wg) {
+                                                         int rows_per_wg, int gr, float theta) {
   __shared__ uint32_t lh[2048];
   const int bh = blockIdx.y;
   if (sel[bh * 4 + 2] == 0) return;
@@ -283,12 +301,14 @@ __global__ __launch_bounds__(256) void slack_hist_kernel(Geo g, const float* __r
   for (int x = threadIdx.x; x < 2048; x += 256) lh[x] = 0u;
   __syncthreads();
   const int i0 = blockIdx.x * rows_per_wg;
-  const int i1 = min(g.nb, i0 + rows_per_wg);
+  const int i1 = min(gr, i0 + rows_per_wg);
   for (int i = i0; i < i1; ++i) {
-    const long row = (long)bh * g.nb + i;
+    const long row = (long)bh * gr + i;
     for (int j = threadIdx.x; j < g.nb; j += 256) {
       if ((bitmap[row * g.words + (j >> 5)] >> (j & 31)) & 1u) continue;
-      const uint32_t key = __float_as_uint(prob[row * g.nb + j]);
+      const float pv = prob[row * g.nb + j];
+      if (!(pv >= theta)) continue;
+      const uint32_t key = __float_as_uint(pv);
       if (pass > 0 && (key >> hshift) != prefix) continue;
       atomicAdd(&lh[(key >> shift) & ((1u << width) - 1u)], 1u);
     }
@@ -313,8 +333,14 @@ __global__ __launch_bounds__(256) void slack_pick_kernel(int* __restrict__ sel,
   for (int e = 0; e < per; ++e) loc += (int)hist[bh * 2048 + nbins - 1 - (threadIdx.x * per + e)];
   int tot;
   const int above = block_exclusive_scan<256>(loc, itmp, &tot);
-  const int need = sel[bh * 4 + 0];
+  int need = sel[bh * 4 + 0];
+  if (pass == 0 && need > tot) need = tot;   // fewer candidates than the budget
   __syncthreads();
+  if (need == 0) {
+    if (threadIdx.x == 0) { sel[bh * 4 + 0] = 0; sel[bh * 4 + 2] = 0; }
+    for (int x = threadIdx.x; x < 2048; x += 256) hist[bh * 2048 + x] = 0u;
+    return;
+  }
   if (above < need && need <= above + loc) {
     int run = above;
     for (int e = 0; e < per; ++e) {
@@ -336,35 +362,38 @@ __global__ __launch_bounds__(256) void slack_pick_kernel(int* __restrict__ sel,
 __global__ __launch_bounds__(256) void slack_eqcount_kernel(Geo g, const float* __restrict__ prob,
                                                             const uint32_t* __restrict__ bitmap,
                                                             const int* __restrict__ sel,
-                                                            int* __restrict__ eqcnt) {
+                                                            int* __restrict__ eqcnt, int gr,
+                                                            float theta) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= g.rows) return;
-  const int bh = row / g.nb;
+  const int bh = row / gr;
   int c = 0;
   if (sel[bh * 4 + 2]) {
     const uint32_t thr = (uint32_t)sel[bh * 4 + 1];
     for (int j = lane; j < g.nb; j += 64) {
       if ((bitmap[(long)row * g.words + (j >> 5)] >> (j & 31)) & 1u) continue;
-      if (__float_as_uint(prob[(long)row * g.nb + j]) == thr) ++c;
+      const float pv = prob[(long)row * g.nb + j];
+      if (pv >= theta && __float_as_uint(pv) == thr) ++c;
     }
   }
   c = wave_sum_int(c);
   if (lane == 0) eqcnt[row] = c;
 }
 
-// Per head: exclusive scan of the per-row equal counts (row order = linear order).
+// Per group: exclusive scan of the per-row equal counts (row order = linear order).
 __global__ __launch_bounds__(256) void slack_eqscan_kernel(Geo g, const int* __restrict__ eqcnt,
-                                                           int* __restrict__ eqoff) {
+                                                           int* __restrict__ eqoff, int gr) {
   __shared__ int itmp[8];
   const int bh = blockIdx.x;
   int carry = 0;
-  for (int base = 0; base < g.nb; base += 256) {
+  for (int base = 0; base < gr; base += 256) {
     const int i = base + threadIdx.x;
-    const int v = i < g.nb ? eqcnt[bh * g.nb + i] : 0;
+    const long r = (long)bh * gr + i;
+    const int v = i < gr ? eqcnt[r] : 0;
     int tot;
     const int ex = block_exclusive_scan<256>(v, itmp, &tot);
-    if (i < g.nb) eqoff[bh * g.nb + i] = carry + ex;
+    if (i < gr) eqoff[r] = carry + ex;
     carry += tot;
   }
 }
@@ -374,11 +403,12 @@ __global__ __launch_bounds__(256) void slack_mark_kernel(Geo g, const float* __r
                                                          uint32_t* __restrict__ bitmap,
                                                          int* __restrict__ count,
                                                          const int* __restrict__ sel,
-                                                         const int* __restrict__ eqoff) {
+                                                         const int* __restrict__ eqoff, int gr,
+                                                         float theta) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= g.rows) return;
-  const int bh = row / g.nb;
+  const int bh = row / gr;
   if (!sel[bh * 4 + 2]) return;
   const uint32_t thr = (uint32_t)sel[bh * 4 + 1];
   const int need_eq = sel[bh * 4 + 0];
@@ -390,8 +420,9 @@ __global__ __launch_bounds__(256) void slack_mark_kernel(Geo g, const float* __r
     bool take = false, eq = false;
     if (j < g.nb) {
       const bool kept = (wp[lane >> 5] >> (lane & 31)) & 1u;
-      if (!kept) {
-        const uint32_t key = __float_as_uint(prob[(long)row * g.nb + j]);
+      const float pv = kept ? 0.f : prob[(long)row * g.nb + j];
+      if (!kept && pv >= theta) {
+        const uint32_t key = __float_as_uint(pv);
         take = key > thr;
         eq = key == thr;
       }
@@ -410,6 +441,56 @@ __global__ __launch_bounds__(256) void slack_mark_kernel(Geo g, const float* __r
     }
   }
   if (lane == 0) count[row] += added;
+}
+
+// ---------------------------------------------------------------------------
+// Dynamic slack budget from the telemetry of one persistent attention launch
+// (one workgroup): records {hw id, xcc id, tiles, busy ticks} per workgroup.
+// T = max busy; idle = n T - sum(busy) ticks, worth idle * sum(tiles) /
+// sum(busy) tiles; budget = floor(fill * that), clamped to [0, max_pairs].
+// The integer product is exact; then one float64 multiply and one divide.
+// Source: FVAttn explainer, "Core method" part 3 (capacity that non-critical
+// workers leave idle after balancing is filled).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void slack_budget_kernel(const long long* __restrict__ telem,
+                                                           int n, float fill, long long max_pairs,
+                                                           long long* __restrict__ budget) {
+  __shared__ long long s_sum[4], s_tiles[4], s_max[4];
+  long long sum = 0, tiles = 0, mx = 0;
+  for (int w = threadIdx.x; w < n; w += 256) {
+    const long long b = telem[4l * w + 3];
+    sum += b;
+    tiles += telem[4l * w + 2];
+    mx = b > mx ? b : mx;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    sum += __shfl_xor(sum, o);
+    tiles += __shfl_xor(tiles, o);
+    const long long om = __shfl_xor(mx, o);
+    mx = om > mx ? om : mx;
+  }
+  if ((threadIdx.x & 63) == 0) {
+    s_sum[threadIdx.x >> 6] = sum;
+    s_tiles[threadIdx.x >> 6] = tiles;
+    s_max[threadIdx.x >> 6] = mx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    sum = tiles = mx = 0;
+    for (int w = 0; w < 4; ++w) {
+      sum += s_sum[w];
+      tiles += s_tiles[w];
+      mx = s_max[w] > mx ? s_max[w] : mx;
+    }
+    long long out = 0;
+    if (sum > 0 && tiles > 0) {
+      const long long idle_tiles = ((long long)n * mx - sum) * tiles;
+      const double v = floor((double)fill * (double)idle_tiles / (double)sum);
+      out = v <= 0.0 ? 0 : (v >= (double)max_pairs ? max_pairs : (long long)v);
+    }
+    *budget = out;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -524,19 +605,71 @@ hipError_t launch_route(const Geo& g, int dtype, const void* q, const void* k, f
     const int rpw = 8;
     for (int pass = 0; pass < 3; ++pass) {
       hipLaunchKernelGGL(slack_hist_kernel, dim3((g.nb + rpw - 1) / rpw, heads), dim3(256), 0, s,
-                         g, score, bm, sel, hist, pass, rpw);
+                         g, score, bm, sel, hist, pass, rpw, g.nb, 0.0f);
       hipLaunchKernelGGL(slack_pick_kernel, dim3(heads), dim3(256), 0, s, sel, hist, pass);
     }
     const int wg4 = (g.rows + 3) / 4;
-    hipLaunchKernelGGL(slack_eqcount_kernel, dim3(wg4), dim3(256), 0, s, g, score, bm, sel, eqcnt);
-    hipLaunchKernelGGL(slack_eqscan_kernel, dim3(heads), dim3(256), 0, s, g, eqcnt, eqoff);
+    hipLaunchKernelGGL(slack_eqcount_kernel, dim3(wg4), dim3(256), 0, s, g, score, bm, sel, eqcnt,
+                       g.nb, 0.0f);
+    hipLaunchKernelGGL(slack_eqscan_kernel, dim3(heads), dim3(256), 0, s, g, eqcnt, eqoff, g.nb);
     hipLaunchKernelGGL(slack_mark_kernel, dim3(wg4), dim3(256), 0, s, g, score, bm, cnt, sel,
-                       eqoff);
+                       eqoff, g.nb, 0.0f);
   }
   hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, s, g, cnt, mask->row_ptr,
                      mask->head_nnz);
   hipLaunchKernelGGL(csr_emit_kernel, dim3((g.rows + 3) / 4), dim3(256), 0, s, g, bm,
                      mask->row_ptr, mask->col_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_dynamic(const Geo& g, int dtype, const void* q, const void* k, float p,
+                                int k_floor, float theta, const long long* budget,
+                                const abs_mask* mask, char* ws, const RouteWs& L, hipStream_t s) {
+  float* qp = (float*)(ws + L.qp);
+  float* kp = (float*)(ws + L.kp);
+  float* score = (float*)(ws + L.score);
+  uint32_t* bm = (uint32_t*)(ws + L.bitmap);
+  int* cnt = (int*)(ws + L.count);
+  if (dtype == ABS_BF16) launch_pool<bf16_t>(g, q, k, qp, kp, s);
+  else launch_pool<float>(g, q, k, qp, kp, s);
+  {
+    dim3 grid((g.nb + 63) / 64, (g.nb + 63) / 64, g.B * g.H);
+    const float scale = (float)(1.0 / sqrt((double)g.d));
+    if (g.d == 128)
+      hipLaunchKernelGGL(scores_kernel<128>, grid, dim3(256), 0, s, g, qp, kp, score, scale);
+    else
+      hipLaunchKernelGGL(scores_kernel<64>, grid, dim3(256), 0, s, g, qp, kp, score, scale);
+  }
+  launch_select(g, score, bm, cnt, p, k_floor, 1, s);
+  // one group: the whole batch
+  uint32_t* hist = (uint32_t*)(ws + L.hist);
+  int* sel = (int*)(ws + L.sel);
+  int* eqcnt = (int*)(ws + L.eqcnt);
+  int* eqoff = (int*)(ws + L.eqoff);
+  hipLaunchKernelGGL(dslack_init_kernel, dim3(1), dim3(256), 0, s, sel, hist, budget);
+  const int rpw = 64;
+  for (int pass = 0; pass < 3; ++pass) {
+    hipLaunchKernelGGL(slack_hist_kernel, dim3((g.rows + rpw - 1) / rpw, 1), dim3(256), 0, s, g,
+                       score, bm, sel, hist, pass, rpw, g.rows, theta);
+    hipLaunchKernelGGL(slack_pick_kernel, dim3(1), dim3(256), 0, s, sel, hist, pass);
+  }
+  const int wg4 = (g.rows + 3) / 4;
+  hipLaunchKernelGGL(slack_eqcount_kernel, dim3(wg4), dim3(256), 0, s, g, score, bm, sel, eqcnt,
+                     g.rows, theta);
+  hipLaunchKernelGGL(slack_eqscan_kernel, dim3(1), dim3(256), 0, s, g, eqcnt, eqoff, g.rows);
+  hipLaunchKernelGGL(slack_mark_kernel, dim3(wg4), dim3(256), 0, s, g, score, bm, cnt, sel, eqoff,
+                     g.rows, theta);
+  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, s, g, cnt, mask->row_ptr,
+                     mask->head_nnz);
+  hipLaunchKernelGGL(csr_emit_kernel, dim3((g.rows + 3) / 4), dim3(256), 0, s, g, bm,
+                     mask->row_ptr, mask->col_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_slack_budget(const long long* telem, int n, float fill, long long max_pairs,
+                               long long* budget, hipStream_t s) {
+  hipLaunchKernelGGL(slack_budget_kernel, dim3(1), dim3(256), 0, s, telem, n, fill, max_pairs,
+                     budget);
   return hipGetLastError();
 }
 

@@ -127,6 +127,13 @@ def main():
     ap.add_argument("--max-parts", type=int, default=None,
                     help="partial-result slots for --split (default: two per persistent "
                          "workgroup)")
+    ap.add_argument("--dynamic-slack", type=float, default=None, metavar="FILL",
+                    help="dynamic slack fill: a base launch's telemetry gives the idle capacity; "
+                         "FILL of it (0..1) is filled with the highest-P unkept pairs")
+    ap.add_argument("--slack-theta", type=float, default=1e-3,
+                    help="score threshold of the dynamic fill (P >= theta)")
+    ap.add_argument("--slack-cap", type=int, default=None,
+                    help="cap on pairs the dynamic fill adds (default: 5%% of the base mask)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--timed-only", action="store_true",
                     help="run only the warmup and timed steps (no schedule sweep, cold step or "
@@ -203,10 +210,42 @@ def main():
         else:
             A.attend_run(plan, q, k, msk, out, s_, aws, telemetry=telemetry)
 
+    # dynamic slack: one base launch's telemetry sets the budget (on the device)
+    dyn = None
+    if args.dynamic_slack is not None:
+        if args.sched == "head_major":
+            print("--dynamic-slack needs a persistent queue", file=sys.stderr)
+            sys.exit(2)
+        A.route(plan, q, k, p, wl.k_floor, wl.slack, mask=mask, ws=rws)
+        base_tiles = mask.nnz()
+        cap = args.slack_cap if args.slack_cap is not None else base_tiles // 20
+        tel0 = torch.zeros(A.attend_grid(plan, sched) * 4, dtype=torch.int64, device=dev)
+        budget_t = torch.zeros(1, dtype=torch.int64, device=dev)
+        prepare(mask, sched)
+        for _ in range(3):
+            run(mask, o, sched)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            run(mask, o, sched)
+        e1.record(stream)
+        run(mask, o, sched, telemetry=tel0)
+        A.slack_budget(plan, sched, tel0, args.dynamic_slack, cap, budget_t)
+        torch.cuda.synchronize()
+        dyn = {"fill": args.dynamic_slack, "theta": args.slack_theta, "cap": cap,
+               "budget": int(budget_t.item()), "base_tiles": base_tiles,
+               "base_ms_attend_kernel": round(e0.elapsed_time(e1) / 5, 4),
+               "base_busy_max_over_mean": round(imbalance(
+                   tel0.cpu().numpy().reshape(-1, 4))["busy_max_over_mean"], 4)}
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        A.route(plan, q, k, p, wl.k_floor, wl.slack, mask=mask, ws=rws)
+        if dyn is not None:
+            A.route_dynamic(plan, q, k, p, wl.k_floor, args.slack_theta, budget_t, mask=mask,
+                            ws=rws)
+        else:
+            A.route(plan, q, k, p, wl.k_floor, wl.slack, mask=mask, ws=rws)
         if ev is not None:
             ev[1].record(stream)
         prepare(mask, sched)
@@ -249,6 +288,14 @@ def main():
 
     # per-CU balance and kernel time under every schedule (the naive
     # head-major hardware dispatch included)
+    if dyn is not None:
+        dyn["added_pairs"] = nnz - dyn["base_tiles"]
+        t_tile = dyn["base_ms_attend_kernel"] / dyn["base_tiles"]
+        dyn["ms_attend_kernel"] = round(float(t_attn), 4)
+        # extra time over the time the added tiles cost at the base launch's mean rate
+        dyn["fill_cost"] = (round((float(t_attn) - dyn["base_ms_attend_kernel"])
+                                  / (dyn["added_pairs"] * t_tile), 3)
+                            if dyn["added_pairs"] > 0 else None)
     bal = {}
     o2 = torch.empty_like(q)
     sweep = {} if args.timed_only else A.SCHEDULES
@@ -358,6 +405,7 @@ def main():
                       "gbs_algorithmic": round(2 * wl.tokens * wl.heads * wl.head_dim * 2
                                                / (t_route * 1e-3) / 1e9, 1)},
         "imbalance": bal,
+        "dynamic_slack": dyn,
         "ms_per_step_cold": round(float(np.median(cold)), 4) if cold else None,
         "dense_p1": dense,
         "cpu_baseline": cpu,

@@ -138,6 +138,43 @@ abs_status abs_route(const abs_plan* plan, const void* q, const void* k, float p
                      int32_t k_floor, float slack, const abs_mask* mask, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* Routing with a dynamic slack fill (explainer "Core method" part 3: after
+ * balancing, workers off the critical path still go idle, and that capacity is
+ * filled with high-scoring blocks; "Lessons for engineering" item 5: only
+ * blocks above a score threshold are used, and the injected amount is the knob
+ * to turn down).  Base routing as abs_route with slack = 0, then, over the
+ * whole batch at once, the unkept pairs with P >= theta are ranked by P
+ * descending (ties: lowest linear index ((b*H + h)*nb + i)*nb + j) and the
+ * first min(*budget, number of such pairs) are added.  The budget is read on
+ * the device, in stream order, so it can come straight from
+ * abs_slack_budget without a host round trip.
+ *   theta  : in [0, 1]
+ *   budget : device int64 [1]; values below 0 count as 0
+ *   ws     : as abs_route (plan->route_ws_bytes); the pooled means are at its
+ *            start on return, as there.
+ * Errors as abs_route, plus ABS_EINVAL for theta outside [0, 1] or a null
+ * budget. */
+abs_status abs_route_dynamic(const abs_plan* plan, const void* q, const void* k, float p,
+                             int32_t k_floor, float theta, const int64_t* budget,
+                             const abs_mask* mask, void* ws, size_t ws_bytes, void* stream);
+
+/* Pair budget for abs_route_dynamic from the telemetry of one persistent
+ * attention launch of this plan (abs_attend_run or abs_attend_run_split with
+ * the same sched; abs_attend_grid(plan, sched) records).  With T = the largest
+ * busy count, idle = sum over workgroups of (T - busy) ticks; at the launch's
+ * mean cost per kept tile this is idle * sum(tiles) / sum(busy) tiles, and
+ * *budget = floor(fill * that) clamped to [0, max_pairs] (integer product,
+ * then one float64 multiply and one divide).  Written on the device in stream
+ * order.
+ *   telemetry : device int64 records as abs_attend_run writes them
+ *   fill      : in [0, 1]; max_pairs >= 0
+ *   budget    : device int64 [1], written
+ * Errors: ABS_EINVAL for a null pointer, sched HEAD_MAJOR (its workgroups are
+ * not persistent workers) or out-of-range fill / max_pairs; ABS_ENOTSUP for
+ * float32 plans (their attention is not persistent). */
+abs_status abs_slack_budget(const abs_plan* plan, int32_t sched, const int64_t* telemetry,
+                            float fill, int64_t max_pairs, int64_t* budget, void* stream);
+
 /* Attention prologue: re-lays k and v block-major for the attention kernel
  * (bf16) and builds the order of `sched` over the attention work items from
  * the mask's row lengths (explainer "Core method" part 2: profile the mask

@@ -150,3 +150,25 @@ def pair_groups(geo, heads: int):
                 partner = bh * geo.nb + i + stride if coord + 1 < n else -1
                 out.append((bh * geo.nb + i, partner))
     return out
+
+
+def check_dynamic_slack(gpu_keep: np.ndarray, gpu_base: np.ndarray, P: np.ndarray, budget: int,
+                        theta: float, tie_rel: float = 1e-5):
+    """GPU dynamic slack fill against the oracle fill applied to the GPU's own
+    base mask.  Pairs chosen differently may only be pairs whose probability is
+    within a relative 1e-5 of the selection threshold or of theta (float32
+    versus float64 probabilities).  The GPU keeps every base pair, and adds as
+    many pairs as the oracle unless a candidate sits at theta.  Returns the
+    number of differing pairs and the oracle's info."""
+    ref, info = O.dynamic_slack_fill(P, gpu_base, budget, theta)
+    assert (gpu_keep[gpu_base]).all(), "base pair dropped"
+    added = int(gpu_keep.sum() - gpu_base.sum())
+    at_theta = np.abs(P[~gpu_base] - theta) <= tie_rel * max(theta, 1e-30)
+    if not at_theta.any():
+        assert added == info["added"], (added, info)
+    d = gpu_keep != ref
+    if d.any():
+        thr = info["last"] if info["added"] else theta
+        near = (np.abs(P[d] - thr) <= tie_rel * thr) | (np.abs(P[d] - theta) <= tie_rel * theta)
+        assert near.all(), (int(d.sum()), P[d][~near][:4], thr, theta)
+    return int(d.sum()), info

@@ -179,3 +179,34 @@ def test_attend_split_workspace_size():
     assert more - base >= 100 * slot
     lib = _lib()
     assert lib.abs_attend_split_ws_bytes(ctypes.byref(plan), 4, None) == A.EINVAL
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(theta=-0.1), A.EINVAL), (dict(theta=1.5), A.EINVAL), (dict(theta=math.nan), A.EINVAL),
+    (dict(budget=None), A.EINVAL), (dict(p=0.0), A.EINVAL), (dict(kf=0), A.EINVAL),
+    (dict(ws_bytes=1024), A.ENOSPACE),
+])
+def test_route_dynamic_validation(kw, want):
+    lib = _lib()
+    plan = _plan()
+    cm = A.CMask(0x100000, 0x200000, 0x300000)
+    budget = kw.get("budget", FAKE)
+    st = lib.abs_route_dynamic(ctypes.byref(plan), FAKE, FAKE, kw.get("p", 0.9), kw.get("kf", 4),
+                               kw.get("theta", 0.01), budget, ctypes.byref(cm), FAKE,
+                               kw.get("ws_bytes", plan.route_ws_bytes), None)
+    assert st == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(sched=A.SCHED_HEAD_MAJOR), A.EINVAL), (dict(sched=7), A.EINVAL),
+    (dict(fill=1.5), A.EINVAL), (dict(fill=-0.5), A.EINVAL), (dict(fill=math.nan), A.EINVAL),
+    (dict(max_pairs=-1), A.EINVAL), (dict(tel=None), A.EINVAL), (dict(out=None), A.EINVAL),
+    (dict(dtype=A.F32), A.ENOTSUP),
+])
+def test_slack_budget_validation(kw, want):
+    lib = _lib()
+    plan = _plan(kw.get("dtype", A.BF16))
+    st = lib.abs_slack_budget(ctypes.byref(plan), kw.get("sched", A.SCHED_XCD_LOCAL),
+                              kw.get("tel", FAKE), kw.get("fill", 0.5), kw.get("max_pairs", 100),
+                              kw.get("out", FAKE), None)
+    assert st == want
