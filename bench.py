@@ -198,43 +198,41 @@ def main():
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
-    def prepare(msk, s_):
+    def prepare(msk, s_, ws_=None):
+        ws_ = aws if ws_ is None else ws_
         if split:
-            A.attend_prepare_split(plan, k, v, msk, s_, args.split, max_parts, aws)
+            A.attend_prepare_split(plan, k, v, msk, s_, args.split, max_parts, ws_)
         else:
-            A.attend_prepare(plan, k, v, msk, s_, aws)
+            A.attend_prepare(plan, k, v, msk, s_, ws_)
 
-    def run(msk, out, s_, telemetry=None):
+    def run(msk, out, s_, telemetry=None, ws_=None):
+        ws_ = aws if ws_ is None else ws_
         if split:
-            A.attend_run_split(plan, q, msk, out, s_, max_parts, aws, telemetry=telemetry)
+            A.attend_run_split(plan, q, msk, out, s_, max_parts, ws_, telemetry=telemetry)
         else:
-            A.attend_run(plan, q, k, msk, out, s_, aws, telemetry=telemetry)
+            A.attend_run(plan, q, k, msk, out, s_, ws_, telemetry=telemetry)
 
     # dynamic slack: one base launch's telemetry sets the budget (on the device)
     dyn = None
+    o2_dyn = torch.empty_like(q) if args.dynamic_slack is not None else None
     if args.dynamic_slack is not None:
         if args.sched == "head_major":
             print("--dynamic-slack needs a persistent queue", file=sys.stderr)
             sys.exit(2)
-        A.route(plan, q, k, p, wl.k_floor, wl.slack, mask=mask, ws=rws)
-        base_tiles = mask.nnz()
+        bmask = A.route(plan, q, k, p, wl.k_floor, wl.slack, ws=rws)   # the base mask
+        base_tiles = bmask.nnz()
         cap = args.slack_cap if args.slack_cap is not None else base_tiles // 20
         tel0 = torch.zeros(A.attend_grid(plan, sched) * 4, dtype=torch.int64, device=dev)
         budget_t = torch.zeros(1, dtype=torch.int64, device=dev)
-        prepare(mask, sched)
+        bws = A.workspace(aws.numel(), dev)
+        prepare(bmask, sched, bws)
         for _ in range(3):
-            run(mask, o, sched)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(5):
-            run(mask, o, sched)
-        e1.record(stream)
-        run(mask, o, sched, telemetry=tel0)
+            run(bmask, o, sched, ws_=bws)
+        run(bmask, o, sched, telemetry=tel0, ws_=bws)
         A.slack_budget(plan, sched, tel0, args.dynamic_slack, cap, budget_t)
         torch.cuda.synchronize()
         dyn = {"fill": args.dynamic_slack, "theta": args.slack_theta, "cap": cap,
                "budget": int(budget_t.item()), "base_tiles": base_tiles,
-               "base_ms_attend_kernel": round(e0.elapsed_time(e1) / 5, 4),
                "base_busy_max_over_mean": round(imbalance(
                    tel0.cpu().numpy().reshape(-1, 4))["busy_max_over_mean"], 4)}
 
@@ -289,13 +287,26 @@ def main():
     # per-CU balance and kernel time under every schedule (the naive
     # head-major hardware dispatch included)
     if dyn is not None:
+        # base and filled masks' attention launches interleaved (each on its own
+        # workspace), so that clock drift affects both alike
         dyn["added_pairs"] = nnz - dyn["base_tiles"]
+        tb, td = [], []
+        for _ in range(6):
+            for msk, ws_, acc in ((bmask, bws, tb), (mask, aws, td)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                run(msk, o2_dyn, sched, ws_=ws_)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                acc.append(e0.elapsed_time(e1))
+        dyn["base_ms_attend_kernel"] = round(float(np.median(tb[1:])), 4)
+        dyn["ms_attend_kernel"] = round(float(np.median(td[1:])), 4)
         t_tile = dyn["base_ms_attend_kernel"] / dyn["base_tiles"]
-        dyn["ms_attend_kernel"] = round(float(t_attn), 4)
-        # extra time over the time the added tiles cost at the base launch's mean rate
-        dyn["fill_cost"] = (round((float(t_attn) - dyn["base_ms_attend_kernel"])
+        # extra time over what the added tiles cost at the base launch's mean rate
+        dyn["fill_cost"] = (round((dyn["ms_attend_kernel"] - dyn["base_ms_attend_kernel"])
                                   / (dyn["added_pairs"] * t_tile), 3)
                             if dyn["added_pairs"] > 0 else None)
+        del bws
     bal = {}
     o2 = torch.empty_like(q)
     sweep = {} if args.timed_only else A.SCHEDULES
