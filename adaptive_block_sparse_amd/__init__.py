@@ -30,7 +30,7 @@ SCHEDULES = {"nnz_sorted": SCHED_NNZ_SORTED, "head_major": SCHED_HEAD_MAJOR,
 EXPORTS = ("abs_plan_init", "abs_route", "abs_attend_prepare", "abs_attend_run",
            "abs_attend", "abs_attend_grid", "abs_status_string", "abs_attend_split_ws_bytes",
            "abs_attend_prepare_split", "abs_attend_run_split", "abs_route_dynamic",
-           "abs_slack_budget")
+           "abs_slack_budget", "abs_attend_relayout", "abs_attend_schedule")
 
 
 class Shape(ctypes.Structure):
@@ -84,6 +84,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "abs_attend_prepare_split": [P, V, V, M, I32, I32, I32, V, SZ, V],
         "abs_attend_run_split": [P, V, M, V, I32, I32, V, SZ, V, V],
         "abs_route_dynamic": [P, V, V, F, I32, F, V, M, V, SZ, V],
+        "abs_attend_relayout": [P, V, V, V, SZ, V],
+        "abs_attend_schedule": [P, M, I32, V, SZ, V],
         "abs_slack_budget": [P, I32, V, F, ctypes.c_int64, V, V],
     }
     for name, args in sig.items():
@@ -225,6 +227,22 @@ def attend_prepare(plan: Plan, k, v, mask: Mask, sched: int, ws, stream=None) ->
     _check("abs_attend_prepare",
            load_library().abs_attend_prepare(ctypes.byref(plan), _ptr(k), _ptr(v), ctypes.byref(cm),
                                              int(sched), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def attend_relayout(plan: Plan, k, v, ws, stream=None) -> None:
+    """The mask-independent half of attend_prepare (K/V re-layout)."""
+    _check_qkv(plan, k, v)
+    _check("abs_attend_relayout",
+           load_library().abs_attend_relayout(ctypes.byref(plan), _ptr(k), _ptr(v), _ptr(ws),
+                                              ws.numel(), _stream(stream)))
+
+
+def attend_schedule(plan: Plan, mask: Mask, sched: int, ws, stream=None) -> None:
+    """The mask-dependent half of attend_prepare (key-block lists, order)."""
+    cm = mask.c()
+    _check("abs_attend_schedule",
+           load_library().abs_attend_schedule(ctypes.byref(plan), ctypes.byref(cm), int(sched),
+                                              _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def attend_run(plan: Plan, q, k, mask: Mask, o, sched: int, ws, telemetry=None,

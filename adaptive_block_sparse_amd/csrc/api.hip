@@ -229,6 +229,29 @@ abs_status abs_attend_prepare(const abs_plan* plan, const void* k, const void* v
   return e == hipSuccess ? ABS_OK : ABS_EHIP;
 }
 
+abs_status abs_attend_relayout(const abs_plan* plan, const void* k, const void* v, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (!plan_ok(plan) || !k || !v || !ws) return ABS_EINVAL;
+  Geo g = make_geo(plan);
+  AttendWs L = attend_ws_layout(g, plan->s.dtype);
+  if (ws_bytes < L.total) return ABS_ENOSPACE;
+  hipError_t e = launch_attend_relayout(g, plan->s.dtype, k, v, (char*)ws, L,
+                                        (hipStream_t)stream);
+  return e == hipSuccess ? ABS_OK : ABS_EHIP;
+}
+
+abs_status abs_attend_schedule(const abs_plan* plan, const abs_mask* mask, int32_t sched,
+                               void* ws, size_t ws_bytes, void* stream) {
+  if (!plan_ok(plan) || !mask_ok(mask) || !ws) return ABS_EINVAL;
+  if (sched < ABS_SCHED_NNZ_SORTED || sched > ABS_SCHED_XCD_LOCAL) return ABS_EINVAL;
+  Geo g = make_geo(plan);
+  AttendWs L = attend_ws_layout(g, plan->s.dtype);
+  if (ws_bytes < L.total) return ABS_ENOSPACE;
+  hipError_t e = launch_attend_schedule(g, plan->s.dtype, mask, sched, plan->heads_per_phase,
+                                        (char*)ws, L, (hipStream_t)stream);
+  return e == hipSuccess ? ABS_OK : ABS_EHIP;
+}
+
 abs_status abs_attend_grid(const abs_plan* plan, int32_t sched, int32_t* workgroups) {
   if (!plan_ok(plan) || !workgroups) return ABS_EINVAL;
   if (sched < ABS_SCHED_NNZ_SORTED || sched > ABS_SCHED_XCD_LOCAL) return ABS_EINVAL;

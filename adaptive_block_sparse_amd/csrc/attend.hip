@@ -1044,9 +1044,8 @@ static void launch_relayout_bf16(const Geo& g, const void* k, const void* v, cha
   }
 }
 
-hipError_t launch_attend_prepare(const Geo& g, int dtype, const void* k, const void* v,
-                                 const abs_mask* mask, int sched, int heads_per_phase, char* ws,
-                                 const AttendWs& L, hipStream_t s) {
+hipError_t launch_attend_relayout(const Geo& g, int dtype, const void* k, const void* v,
+                                  char* ws, const AttendWs& L, hipStream_t s) {
   if (dtype == ABS_BF16) {
     launch_relayout_bf16(g, k, v, ws, L, s);
   } else {
@@ -1055,6 +1054,20 @@ hipError_t launch_attend_prepare(const Geo& g, int dtype, const void* k, const v
     hipError_t e = hipMemcpyAsync(ws + L.vc, v, bytes, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_prepare(const Geo& g, int dtype, const void* k, const void* v,
+                                 const abs_mask* mask, int sched, int heads_per_phase, char* ws,
+                                 const AttendWs& L, hipStream_t s) {
+  hipError_t e = launch_attend_relayout(g, dtype, k, v, ws, L, s);
+  if (e != hipSuccess) return e;
+  return launch_attend_schedule(g, dtype, mask, sched, heads_per_phase, ws, L, s);
+}
+
+hipError_t launch_attend_schedule(const Geo& g, int dtype, const abs_mask* mask, int sched,
+                                  int heads_per_phase, char* ws, const AttendWs& L,
+                                  hipStream_t s) {
   if (dtype == ABS_BF16)
     hipLaunchKernelGGL(tile_list_kernel, dim3(g.groups), dim3(256), 0, s, g, mask->row_ptr,
                        mask->col_idx, tlist_cap(g), (int*)(ws + L.tlist), (int*)(ws + L.tcount));

@@ -89,6 +89,11 @@ hipError_t launch_route_dynamic(const Geo& g, int dtype, const void* q, const vo
                                 const abs_mask* mask, char* ws, const RouteWs& L, hipStream_t s);
 hipError_t launch_slack_budget(const long long* telem, int n, float fill, long long max_pairs,
                                long long* budget, hipStream_t s);
+hipError_t launch_attend_relayout(const Geo& g, int dtype, const void* k, const void* v,
+                                  char* ws, const AttendWs& L, hipStream_t s);
+hipError_t launch_attend_schedule(const Geo& g, int dtype, const abs_mask* mask, int sched,
+                                  int heads_per_phase, char* ws, const AttendWs& L,
+                                  hipStream_t s);
 hipError_t launch_attend_prepare(const Geo& g, int dtype, const void* k, const void* v,
                                  const abs_mask* mask,
                                  int sched, int heads_per_phase, char* ws, const AttendWs& L,

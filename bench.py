@@ -134,6 +134,9 @@ def main():
                     help="score threshold of the dynamic fill (P >= theta)")
     ap.add_argument("--slack-cap", type=int, default=None,
                     help="cap on pairs the dynamic fill adds (default: 5%% of the base mask)")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="run the K/V re-layout after routing on one stream instead of "
+                         "beside it on a second stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--timed-only", action="store_true",
                     help="run only the warmup and timed steps (no schedule sweep, cold step or "
@@ -236,9 +239,20 @@ def main():
                "base_busy_max_over_mean": round(imbalance(
                    tel0.cpu().numpy().reshape(-1, 4))["busy_max_over_mean"], 4)}
 
+    # the K/V re-layout does not depend on the mask: it runs on a second stream
+    # (default priority) beside the routing, joined before the schedule
+    overlap = not split and not args.no_overlap
+    side = torch.cuda.Stream(device=dev)
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
+        if overlap:
+            fork.record(stream)            # after the previous step's attention
+            side.wait_event(fork)
+            A.attend_relayout(plan, k, v, aws, stream=side)
+            join.record(side)
         if dyn is not None:
             A.route_dynamic(plan, q, k, p, wl.k_floor, args.slack_theta, budget_t, mask=mask,
                             ws=rws)
@@ -246,7 +260,11 @@ def main():
             A.route(plan, q, k, p, wl.k_floor, wl.slack, mask=mask, ws=rws)
         if ev is not None:
             ev[1].record(stream)
-        prepare(mask, sched)
+        if overlap:
+            stream.wait_event(join)
+            A.attend_schedule(plan, mask, sched, aws)
+        else:
+            prepare(mask, sched)
         if ev is not None:
             ev[2].record(stream)
         run(mask, o, sched)
@@ -394,6 +412,7 @@ def main():
                    "p": p, "k_floor": wl.k_floor, "slack": wl.slack, "sched": args.sched,
                    "split": ({"split_tiles": args.split, "max_parts": max_parts} if split
                              else None),
+                   "relayout_beside_route": overlap,
                    "kept_tiles": nnz, "density": round(nnz / (rp.size - 1) / nb, 4),
                    "head_density_min_median_max": [round(float(dens.min()), 4),
                                                    round(float(np.median(dens)), 4),

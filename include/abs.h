@@ -192,6 +192,19 @@ abs_status abs_attend_prepare(const abs_plan* plan, const void* k, const void* v
                               const abs_mask* mask, int32_t sched, void* ws, size_t ws_bytes,
                               void* stream);
 
+/* The two halves of abs_attend_prepare, for callers that overlap the first
+ * with routing (it does not depend on the mask).  abs_attend_relayout does the
+ * K/V re-layout (bf16) or the V copy (float32) into ws; abs_attend_schedule
+ * builds the work items' key-block lists and the order of `sched` from the
+ * mask.  Both, in either order or on different streams, followed by
+ * abs_attend_run in stream order after both (the caller orders the streams,
+ * for instance with events), leave ws exactly as abs_attend_prepare does.
+ * Arguments and errors as abs_attend_prepare. */
+abs_status abs_attend_relayout(const abs_plan* plan, const void* k, const void* v, void* ws,
+                               size_t ws_bytes, void* stream);
+abs_status abs_attend_schedule(const abs_plan* plan, const abs_mask* mask, int32_t sched,
+                               void* ws, size_t ws_bytes, void* stream);
+
 /* Block-sparse attention over the kept blocks (explainer "Core method" part 1
  * and "The real problem"): for each real query token of block i, one softmax
  * over the real keys of all kept blocks of row (b, h, i), scale 1/sqrt(d),

@@ -313,3 +313,30 @@ def test_full_workload_parity(cfg, p):
         for s in (A.SCHED_NNZ_SORTED, A.SCHED_HEAD_MAJOR):
             o2 = _run(wl, p, wl.k_floor, sched=s, inputs=inputs)["o"]
             assert np.array_equal(o2, r["o"])
+
+
+def test_relayout_beside_routing_on_a_second_stream():
+    """abs_attend_relayout on a second stream, overlapping abs_route, then
+    abs_attend_schedule and the run after an event join: the same bits as
+    abs_attend on one stream."""
+    wl = SMALL["bf16-d128-bt128-ragged"]
+    inputs = si.make_inputs(wl)
+    want = _run(wl, 0.9, 2, sched=A.SCHED_XCD_LOCAL, inputs=inputs)["o"]
+    q, k, v = (t.to(DEV) for t in inputs)
+    plan = A.plan_init(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.block, wl.dtype)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    ws = A.workspace(plan.attend_ws_bytes, DEV)
+    o = torch.empty_like(q)
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+    for _ in range(2):                       # the second pass reuses the workspace
+        fork.record(main)
+        side.wait_event(fork)
+        A.attend_relayout(plan, k, v, ws, stream=side)
+        join.record(side)
+        mask = A.route(plan, q, k, 0.9, 2)
+        main.wait_event(join)
+        A.attend_schedule(plan, mask, A.SCHED_XCD_LOCAL, ws)
+        A.attend_run(plan, q, k, mask, o, A.SCHED_XCD_LOCAL, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(o.float().cpu().numpy(), want)

@@ -210,3 +210,18 @@ def test_slack_budget_validation(kw, want):
                               kw.get("tel", FAKE), kw.get("fill", 0.5), kw.get("max_pairs", 100),
                               kw.get("out", FAKE), None)
     assert st == want
+
+
+def test_relayout_and_schedule_validation():
+    lib = _lib()
+    plan = _plan()
+    cm = A.CMask(0x100000, 0x200000, 0x300000)
+    assert lib.abs_attend_relayout(ctypes.byref(plan), None, FAKE, FAKE,
+                                   plan.attend_ws_bytes, None) == A.EINVAL
+    assert lib.abs_attend_relayout(ctypes.byref(plan), FAKE, FAKE, FAKE, 1024, None) == A.ENOSPACE
+    assert lib.abs_attend_schedule(ctypes.byref(plan), ctypes.byref(cm), 9, FAKE,
+                                   plan.attend_ws_bytes, None) == A.EINVAL
+    assert lib.abs_attend_schedule(ctypes.byref(plan), None, 0, FAKE,
+                                   plan.attend_ws_bytes, None) == A.EINVAL
+    assert lib.abs_attend_schedule(ctypes.byref(plan), ctypes.byref(cm), 0, FAKE, 1024,
+                                   None) == A.ENOSPACE
