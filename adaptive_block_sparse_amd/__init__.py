@@ -30,7 +30,8 @@ SCHEDULES = {"nnz_sorted": SCHED_NNZ_SORTED, "head_major": SCHED_HEAD_MAJOR,
 EXPORTS = ("abs_plan_init", "abs_route", "abs_attend_prepare", "abs_attend_run",
            "abs_attend", "abs_attend_grid", "abs_status_string", "abs_attend_split_ws_bytes",
            "abs_attend_prepare_split", "abs_attend_run_split", "abs_route_dynamic",
-           "abs_slack_budget", "abs_attend_relayout", "abs_attend_schedule")
+           "abs_slack_budget", "abs_attend_relayout", "abs_attend_schedule",
+           "abs_attend_default_sched")
 
 
 class Shape(ctypes.Structure):
@@ -80,6 +81,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "abs_attend_run": [P, V, V, M, V, I32, V, SZ, V, V],
         "abs_attend": [P, V, V, V, M, V, I32, V, SZ, V, V],
         "abs_attend_grid": [P, I32, ctypes.POINTER(I32)],
+        "abs_attend_default_sched": [P, ctypes.POINTER(I32)],
         "abs_attend_split_ws_bytes": [P, I32, ctypes.POINTER(SZ)],
         "abs_attend_prepare_split": [P, V, V, M, I32, I32, I32, V, SZ, V],
         "abs_attend_run_split": [P, V, M, V, I32, I32, V, SZ, V, V],
@@ -221,6 +223,14 @@ def attend_grid(plan: Plan, sched: int = SCHED_NNZ_SORTED) -> int:
     return int(n.value)
 
 
+def default_sched(plan: Plan) -> int:
+    """The schedule measured fastest for this plan's shape."""
+    n = ctypes.c_int32(0)
+    _check("abs_attend_default_sched",
+           load_library().abs_attend_default_sched(ctypes.byref(plan), ctypes.byref(n)))
+    return int(n.value)
+
+
 def attend_prepare(plan: Plan, k, v, mask: Mask, sched: int, ws, stream=None) -> None:
     _check_qkv(plan, k, v)
     cm = mask.c()
@@ -256,11 +266,12 @@ def attend_run(plan: Plan, q, k, mask: Mask, o, sched: int, ws, telemetry=None,
                                          _stream(stream)))
 
 
-def attend(plan: Plan, q, k, v, mask: Mask, sched: int = SCHED_XCD_LOCAL, o=None, ws=None,
+def attend(plan: Plan, q, k, v, mask: Mask, sched: Optional[int] = None, o=None, ws=None,
            telemetry=None, stream=None):
     """Block-sparse attention over the kept blocks; returns o [B, N, H, d].
-    The default queue places whole heads on XCDs (the fastest measured)."""
+    The default queue is default_sched(plan), the fastest measured for the shape."""
     torch = _check_qkv(plan, q, k, v)
+    sched = default_sched(plan) if sched is None else sched
     o = torch.empty_like(q) if o is None else o
     ws = workspace(plan.attend_ws_bytes, q.device) if ws is None else ws
     attend_prepare(plan, k, v, mask, sched, ws, stream)

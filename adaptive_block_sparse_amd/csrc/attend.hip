@@ -67,15 +67,25 @@ __global__ __launch_bounds__(256) void kv_relayout_kernel(Geo g, const bf16_t* _
             Wl = min(g.bw, g.W - wb * g.bw);
   const int plane = g.bh * g.bw;
   const bf16_t* src = which == 0 ? k : v;
-  for (int e = threadIdx.x; e < BT * (D / 8); e += 256) {
+  // every load of this thread is issued before the first LDS store
+  constexpr int NIT = (BT * (D / 8) + 255) / 256;
+  uint4 val[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int e = threadIdx.x + 256 * it;
     const int s = e / (D / 8), c = e % (D / 8);
     const int st = s / plane, sh = (s / g.bw) % g.bh, sw = s % g.bw;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (st < Tl && sh < Hl && sw < Wl) {
+    val[it] = make_uint4(0, 0, 0, 0);
+    if (e < BT * (D / 8) && st < Tl && sh < Hl && sw < Wl) {
       const long n = ((long)(tb * g.bt + st) * g.Hg + hb * g.bh + sh) * g.W + wb * g.bw + sw;
-      val = *reinterpret_cast<const uint4*>(src + (((long)b * g.N + n) * g.H + h) * D + c * 8);
+      val[it] = *reinterpret_cast<const uint4*>(src + (((long)b * g.N + n) * g.H + h) * D + c * 8);
     }
-    *reinterpret_cast<uint4*>(&tile[s * RW + c * 4]) = val;
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int e = threadIdx.x + 256 * it;
+    if (e < BT * (D / 8))
+      *reinterpret_cast<uint4*>(&tile[(e / (D / 8)) * RW + (e % (D / 8)) * 4]) = val[it];
   }
   __syncthreads();
   const long tile_off = ((long)bh * g.nb + blk) * (long)(D * BT);

@@ -19,11 +19,21 @@ template <> struct Chunk<float> {
     float4 v = *reinterpret_cast<const float4*>(p);
     out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
   }
+  __device__ __forceinline__ static void unpack(uint4 v, float* out) {
+    out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+    out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
+  }
 };
 template <> struct Chunk<bf16_t> {
   static constexpr int E = 8;
   __device__ __forceinline__ static void load(const bf16_t* p, float* out) {
     uint4 v = *reinterpret_cast<const uint4*>(p);
+    out[0] = bf16_lo(v.x); out[1] = bf16_hi(v.x);
+    out[2] = bf16_lo(v.y); out[3] = bf16_hi(v.y);
+    out[4] = bf16_lo(v.z); out[5] = bf16_hi(v.z);
+    out[6] = bf16_lo(v.w); out[7] = bf16_hi(v.w);
+  }
+  __device__ __forceinline__ static void unpack(uint4 v, float* out) {
     out[0] = bf16_lo(v.x); out[1] = bf16_hi(v.x);
     out[2] = bf16_lo(v.y); out[3] = bf16_hi(v.y);
     out[4] = bf16_lo(v.z); out[5] = bf16_hi(v.z);

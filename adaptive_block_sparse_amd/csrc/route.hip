@@ -42,15 +42,27 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo g, const T* __restrict__ 
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    for (int s = grp; s < g.Bt; s += G) {
-      const int st = s / plane, sh = (s / g.bw) % g.bh, sw = s % g.bw;
-      if (st < Tl && sh < Hl && sw < Wl) {
-        const long n = ((long)(tb * g.bt + st) * g.Hg + hb * g.bh + sh) * g.W + wb * g.bw + sw;
-        float v[E];
-        Chunk<T>::load(src + (((long)b * g.N + n) * g.H + h) * D + c * E, v);
+    // every load of this thread is issued before the first sum (the slots a
+    // thread visits are at most 128 / G); padding slots contribute zeros, and
+    // the sums run in slot order
+    constexpr int MAXIT = 128 / G;
+    uint4 raw[MAXIT];
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] += v[e];
+    for (int it = 0; it < MAXIT; ++it) {
+      const int s = grp + it * G;
+      raw[it] = make_uint4(0u, 0u, 0u, 0u);
+      const int st = s / plane, sh = (s / g.bw) % g.bh, sw = s % g.bw;
+      if (s < g.Bt && st < Tl && sh < Hl && sw < Wl) {
+        const long n = ((long)(tb * g.bt + st) * g.Hg + hb * g.bh + sh) * g.W + wb * g.bw + sw;
+        raw[it] = *reinterpret_cast<const uint4*>(src + (((long)b * g.N + n) * g.H + h) * D + c * E);
       }
+    }
+#pragma unroll
+    for (int it = 0; it < MAXIT; ++it) {
+      float v[E];
+      Chunk<T>::unpack(raw[it], v);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += v[e];
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) red[grp][c * E + e] = acc[e];

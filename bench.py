@@ -120,7 +120,8 @@ def main():
                          "the layer is sharded by head across GPUs)")
     ap.add_argument("--sched", default=None,
                     choices=["nnz_sorted", "head_major", "head_phased", "xcd_local"],
-                    help="work order (default xcd_local; head_phased with --split)")
+                    help="work order (default: the library's choice for the shape; "
+                         "head_phased with --split)")
     ap.add_argument("--split", type=int, default=None,
                     help="split-and-merge attention: cut work items whose union list is longer "
                          "than SPLIT entries into parts, merge the parts by log-sum-exp")
@@ -177,17 +178,18 @@ def main():
         wl = dataclasses.replace(wl, heads=args.heads, name=f"{wl.name}-first{args.heads}heads")
     p = float(np.float32(args.p if args.p is not None else wl.p[0]))
     split = args.split is not None
-    if args.sched is None:
-        args.sched = "head_phased" if split else "xcd_local"
-    if split and args.sched not in ("nnz_sorted", "head_phased"):
+    if split and args.sched not in (None, "nnz_sorted", "head_phased"):
         print("--split runs on the sorted queues: --sched nnz_sorted or head_phased",
               file=sys.stderr)
         sys.exit(2)
-    sched = A.SCHEDULES[args.sched]
     print(f"[bench] generating {wl.name}", file=sys.stderr, flush=True)
     inputs = si.make_inputs(wl)
     q, k, v = (t.to(dev) for t in inputs)
     plan = A.plan_init(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.block, wl.dtype)
+    if args.sched is None:
+        args.sched = "head_phased" if split else {v_: k_ for k_, v_ in A.SCHEDULES.items()}[
+            A.default_sched(plan)]
+    sched = A.SCHEDULES[args.sched]
     mask = A.Mask(plan, dev)
     rws = A.workspace(plan.route_ws_bytes, dev)
     max_parts = 0

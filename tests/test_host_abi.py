@@ -225,3 +225,14 @@ def test_relayout_and_schedule_validation():
                                    plan.attend_ws_bytes, None) == A.EINVAL
     assert lib.abs_attend_schedule(ctypes.byref(plan), ctypes.byref(cm), 0, FAKE, 1024,
                                    None) == A.ENOSPACE
+
+
+@pytest.mark.parametrize("cfg,want", [(1, A.SCHED_XCD_LOCAL), (3, A.SCHED_XCD_LOCAL),
+                                      (2, A.SCHED_HEAD_PHASED), (4, A.SCHED_HEAD_PHASED),
+                                      (0, A.SCHED_HEAD_PHASED)])
+def test_default_sched(cfg, want):
+    _lib()
+    wl = si.WORKLOADS[cfg]
+    plan = A.plan_init(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.block, wl.dtype)
+    assert A.default_sched(plan) == want
+    assert _lib().abs_attend_default_sched(ctypes.byref(plan), None) == A.EINVAL
