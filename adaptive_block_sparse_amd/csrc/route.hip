@@ -244,6 +244,127 @@ __global__ __launch_bounds__(256) void select_kernel(Geo g, float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// The same per-row selection with one wave per row (nb <= 512), no LDS sort
+// and no workgroup barriers: element e = lane * KPL + r of the row lives in
+// register r of lane `lane`, and the bitonic network compares in registers for
+// strides below KPL and across lanes (shuffles) above.  Same keys, so the same
+// order; the float32 sums run in another order than the workgroup version.
+// ---------------------------------------------------------------------------
+template <int NBP>
+__global__ __launch_bounds__(256) void select_wave_kernel(Geo g, float* __restrict__ score,
+                                                          uint32_t* __restrict__ bitmap,
+                                                          int* __restrict__ count, float p,
+                                                          int k_floor, int write_prob) {
+  constexpr int KPL = NBP / 64;   // keys per lane
+  static_assert(KPL >= 1 && KPL <= 8, "one wave per row up to 512 blocks");
+  __shared__ uint32_t bits[4][NBP / 32 > 1 ? NBP / 32 : 1];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + wv;
+  if (row >= g.rows) return;   // whole wave: no workgroup barrier below
+  const int nb = g.nb;
+  const int i = row % nb;
+  float* srow = score + (long)row * nb;
+  float sv[KPL];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) {
+    const int j = lane * KPL + r;
+    sv[r] = j < nb ? srow[j] : -INFINITY;
+    mx = fmaxf(mx, sv[r]);
+  }
+  mx = wave_max(mx);
+  float part = 0.f;
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) {
+    const int j = lane * KPL + r;
+    sv[r] = j < nb ? expf(sv[r] - mx) : 0.f;
+    part += sv[r];
+  }
+  const float z = wave_sum(part);
+  unsigned long long key[KPL];
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) {
+    const int j = lane * KPL + r;
+    key[r] = ~0ull;
+    if (j < nb) {
+      const float pj = sv[r] / z;
+      if (write_prob) srow[j] = pj;
+      key[r] = ((unsigned long long)(~__float_as_uint(pj)) << 32) | (unsigned)j;
+    }
+  }
+  // bitonic sort, ascending keys = P descending then index ascending
+#pragma unroll
+  for (int size = 2; size <= NBP; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride >= KPL) {
+        const int ls = stride / KPL;
+#pragma unroll
+        for (int r = 0; r < KPL; ++r) {
+          const unsigned long long o = __shfl_xor(key[r], ls);
+          const int e = lane * KPL + r;
+          const bool lower = (e & stride) == 0, up = (e & size) == 0;
+          const unsigned long long lo = key[r] < o ? key[r] : o, hi = key[r] < o ? o : key[r];
+          key[r] = (lower == up) ? lo : hi;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < KPL; ++r) {
+          if (r & stride) continue;
+          const int e = lane * KPL + r;
+          const bool up = (e & size) == 0;
+          const unsigned long long a = key[r], c = key[r + stride];
+          if ((a > c) == up) { key[r] = c; key[r + stride] = a; }
+        }
+      }
+    }
+  }
+  // inclusive scan of the sorted masses; first position reaching p
+  float loc[KPL];
+  float run = 0.f;
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) {
+    const int e = lane * KPL + r;
+    run += (e < nb) ? __uint_as_float(~(uint32_t)(key[r] >> 32)) : 0.f;
+    loc[r] = run;
+  }
+  const float pre = wave_inclusive_scan(run) - run;
+  int first = nb;
+#pragma unroll
+  for (int r = KPL - 1; r >= 0; --r) {
+    const int e = lane * KPL + r;
+    if (e < nb && pre + loc[r] >= p) first = e + 1;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o));
+  const int m = (p >= 1.0f) ? nb : first;
+  const int m2 = min(nb, max(m, k_floor));
+  uint32_t* wb = bits[wv];
+  for (int w = lane; w < NBP / 32; w += 64) wb[w] = 0u;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) {
+    const int e = lane * KPL + r;
+    if (e < m2) {
+      const int j = (int)(key[r] & 0xffffffffu);
+      atomicOr(&wb[j >> 5], 1u << (j & 31));
+    }
+  }
+  if (lane == 0) atomicOr(&wb[i >> 5], 1u << (i & 31));
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  int pc = 0;
+  for (int w = lane; w < g.words; w += 64) {
+    const uint32_t v = wb[w];
+    bitmap[(long)row * g.words + w] = v;
+    pc += __popc(v);
+  }
+  pc = wave_sum_int(pc);
+  if (lane == 0) count[row] = pc;
+}
+
+// ---------------------------------------------------------------------------
 // Slack fill over groups of gr consecutive rows: in each group, add the `need`
 // unkept pairs with the largest P among those with P >= theta (ties: lowest
 // linear index).  Exact selection by a three-pass radix select on the float
@@ -575,12 +696,19 @@ static void launch_select_n(const Geo& g, float* score, uint32_t* bm, int* cnt, 
                      kf, wp);
 }
 
+template <int NBP>
+static void launch_select_wave(const Geo& g, float* score, uint32_t* bm, int* cnt, float p,
+                               int kf, int wp, hipStream_t s) {
+  hipLaunchKernelGGL((select_wave_kernel<NBP>), dim3((g.rows + 3) / 4), dim3(256), 0, s, g, score,
+                     bm, cnt, p, kf, wp);
+}
+
 static void launch_select(const Geo& g, float* score, uint32_t* bm, int* cnt, float p, int kf,
                           int wp, hipStream_t s) {
-  if (g.nb <= 64) launch_select_n<64>(g, score, bm, cnt, p, kf, wp, s);
-  else if (g.nb <= 128) launch_select_n<128>(g, score, bm, cnt, p, kf, wp, s);
-  else if (g.nb <= 256) launch_select_n<256>(g, score, bm, cnt, p, kf, wp, s);
-  else if (g.nb <= 512) launch_select_n<512>(g, score, bm, cnt, p, kf, wp, s);
+  if (g.nb <= 64) launch_select_wave<64>(g, score, bm, cnt, p, kf, wp, s);
+  else if (g.nb <= 128) launch_select_wave<128>(g, score, bm, cnt, p, kf, wp, s);
+  else if (g.nb <= 256) launch_select_wave<256>(g, score, bm, cnt, p, kf, wp, s);
+  else if (g.nb <= 512) launch_select_wave<512>(g, score, bm, cnt, p, kf, wp, s);
   else if (g.nb <= 1024) launch_select_n<1024>(g, score, bm, cnt, p, kf, wp, s);
   else if (g.nb <= 2048) launch_select_n<2048>(g, score, bm, cnt, p, kf, wp, s);
   else launch_select_n<4096>(g, score, bm, cnt, p, kf, wp, s);
