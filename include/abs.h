@@ -14,7 +14,12 @@
  *           kernel runs and give the heaviest work out first (here: across the
  *           compute units of one GPU instead of across ranks);
  *   part 3, slack-aware augmentation: fill spare capacity with the highest
- *           scoring blocks (here: a fixed per-head block budget).
+ *           scoring blocks (here: a fixed per-head block budget, or a budget
+ *           derived on the device from the idle time a persistent launch
+ *           measured, abs_slack_budget / abs_route_dynamic).
+ * Heavy work items can also be cut into parts whose partial softmax results
+ * are merged by log-sum-exp (abs_attend_*_split), the merge the APB-V paper
+ * notes use across hosts.
  *
  * Tensor layout.  q, k, v and o are contiguous [B, N, H, d] with the N = T*H*W
  * latent tokens in row-major (t, h, w) order, the layout a DiT's QKV projection
@@ -32,7 +37,7 @@
  * the device.  ABS_EHIP reports a launch error from the HIP runtime.  Nothing
  * throws across this interface.  Calls on distinct streams with distinct
  * workspaces are independent (the library holds no mutable global state apart
- * from a per-device cache of the compute-unit count).
+ * from a per-device cache of the compute-unit count and occupancy).
  */
 #ifndef ABS_H
 #define ABS_H
