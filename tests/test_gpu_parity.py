@@ -49,11 +49,14 @@ SMALL = {
 }
 
 
-def _run(wl, p, k_floor, slack=0.0, sched=A.SCHED_HEAD_PHASED, inputs=None, telemetry=False):
-    print(f"[gpu case] {wl.name} p={p} k_floor={k_floor} slack={slack} sched={sched}", flush=True)
+def _run(wl, p, k_floor, slack=0.0, sched=None, inputs=None, telemetry=False):
+    """Route and attend; sched None = the library's default for the shape (the
+    schedule the benchmark times)."""
     q, k, v = inputs if inputs is not None else si.make_inputs(wl)
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
     plan = A.plan_init(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.block, wl.dtype)
+    sched = A.default_sched(plan) if sched is None else sched
+    print(f"[gpu case] {wl.name} p={p} k_floor={k_floor} slack={slack} sched={sched}", flush=True)
     mask = A.route(plan, qd, kd, p, k_floor, slack)
     tel = None
     if telemetry:
@@ -86,7 +89,8 @@ def test_small_full_parity(name):
     print("max/mean err", compare_outputs(r["o"], o_ref, geo, rows, wl.heads, wl.dtype))
     assert r["tel"][:, 2].sum() == ci.size          # every kept tile done exactly once
     # every schedule gives the same bits
-    for sched in (A.SCHED_NNZ_SORTED, A.SCHED_HEAD_MAJOR, A.SCHED_XCD_LOCAL):
+    for sched in (A.SCHED_NNZ_SORTED, A.SCHED_HEAD_MAJOR, A.SCHED_HEAD_PHASED,
+                  A.SCHED_XCD_LOCAL):
         o2 = _run(wl, p, wl.k_floor, sched=sched, inputs=(r["q"], r["k"], r["v"]))["o"]
         assert np.array_equal(o2, r["o"])
 
@@ -309,10 +313,30 @@ def test_full_workload_parity(cfg, p):
     o_ref = O.sparse_attention(q, k, v, geo, rp, ci, rows=rows)
     print("max/mean err", compare_outputs(r["o"], o_ref, geo, rows, wl.heads, wl.dtype))
     if cfg == 1:
-        # the same item outputs under the other two schedules, bitwise
-        for s in (A.SCHED_NNZ_SORTED, A.SCHED_HEAD_MAJOR):
+        # the same outputs under the other schedules, bitwise
+        for s in (A.SCHED_NNZ_SORTED, A.SCHED_HEAD_MAJOR, A.SCHED_HEAD_PHASED,
+                  A.SCHED_XCD_LOCAL):
             o2 = _run(wl, p, wl.k_floor, sched=s, inputs=inputs)["o"]
             assert np.array_equal(o2, r["o"])
+        # and the benchmark's pipeline: the K/V re-layout on a second stream
+        # beside routing, joined by an event before the schedule
+        qd, kd, vd = (t.to(DEV) for t in inputs)
+        plan = r["plan"]
+        sched = A.default_sched(plan)
+        main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+        ws = A.workspace(plan.attend_ws_bytes, DEV)
+        o3 = torch.empty_like(qd)
+        fork, join = torch.cuda.Event(), torch.cuda.Event()
+        fork.record(main)
+        side.wait_event(fork)
+        A.attend_relayout(plan, kd, vd, ws, stream=side)
+        join.record(side)
+        m3 = A.route(plan, qd, kd, p, wl.k_floor)
+        main.wait_event(join)
+        A.attend_schedule(plan, m3, sched, ws)
+        A.attend_run(plan, qd, kd, m3, o3, sched, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(o3.float().cpu().numpy(), r["o"])
 
 
 def test_relayout_beside_routing_on_a_second_stream():
