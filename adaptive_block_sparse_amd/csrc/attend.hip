@@ -290,31 +290,18 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
 // Per attention work item (a pair of query blocks of one head, or a single
 // block), the union of its rows' kept key-block lists in ascending order, each
 // entry j | (kept by the first block) << 17 | (kept by the second) << 18.  One
-// workgroup per item.  The two ascending lists are merged by rank: an element
-// of the first list goes to its index plus the number of elements of the
-// second list below it, an element of the second list to its index plus the
-// number of elements of the first list at or below it; the second copy of a
-// block both rows keep is marked, and a block-wide scan compacts the rest.
-// The list of item i starts at tlist[i * cap], cap = 2 nb, with tcount[i]
-// entries.
+// workgroup per item: the two rows are marked in two LDS bitmaps of nb bits,
+// thread w takes word w of their union, and a workgroup scan of the words'
+// popcounts places each word's blocks, in ascending order, in the list.  The
+// list of item i starts at tlist[i * cap], cap = 2 nb, with tcount[i] entries.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int rank_below(const int* x, int n, int v, bool inclusive) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    const int xm = x[mid];
-    if (xm < v || (inclusive && xm == v)) lo = mid + 1;
-    else hi = mid;
-  }
-  return lo;
-}
-
 __global__ __launch_bounds__(256) void tile_list_kernel(Geo g, const int* __restrict__ row_ptr,
                                                         const int* __restrict__ col_idx, int cap,
                                                         int* __restrict__ tlist,
                                                         int* __restrict__ tcount) {
-  constexpr int NT = 256;
-  __shared__ int merged[2 * MAX_NB];   // j | owners << 17, or -1 for a dropped second copy
+  constexpr int NT = 256, MAXW = MAX_NB / 32;
+  static_assert(MAXW <= NT, "one bitmap word per thread");
+  __shared__ uint32_t bA[MAXW], bB[MAXW];
   __shared__ int tmp[NT / 64 + 1];
   const int item = blockIdx.x;
   const int bhh = item / g.groups_per_head, gl = item % g.groups_per_head;
@@ -328,33 +315,31 @@ __global__ __launch_bounds__(256) void tile_list_kernel(Geo g, const int* __rest
     pB = row_ptr[rB];
     nB = row_ptr[rB + 1] - pB;
   }
-  const int* A = col_idx + pA;
-  const int* Bl = col_idx + pB;
+  const int W = (g.nb + 31) / 32;
+  for (int w = threadIdx.x; w < W; w += NT) { bA[w] = 0u; bB[w] = 0u; }
+  __syncthreads();
   for (int i = threadIdx.x; i < nA; i += NT) {
-    const int v = A[i];
-    const int r = rank_below(Bl, nB, v, false);
-    const bool both = r < nB && Bl[r] == v;
-    merged[i + r] = v | ((both ? 3 : 1) << 17);
+    const int v = col_idx[pA + i];
+    atomicOr(&bA[v >> 5], 1u << (v & 31));
   }
   for (int i = threadIdx.x; i < nB; i += NT) {
-    const int v = Bl[i];
-    const int r = rank_below(A, nA, v, true);
-    const bool both = r > 0 && A[r - 1] == v;
-    merged[i + r] = both ? -1 : (v | (2 << 17));
+    const int v = col_idx[pB + i];
+    atomicOr(&bB[v >> 5], 1u << (v & 31));
   }
   __syncthreads();
-  const int n = nA + nB;
+  const int w = threadIdx.x;
+  const uint32_t a = w < W ? bA[w] : 0u, b = w < W ? bB[w] : 0u;
+  uint32_t u = a | b;
+  int tot;
+  int off = block_exclusive_scan<NT>((int)__popc(u), tmp, &tot);
   int* out = tlist + (long)item * cap;
-  int base = 0;
-  for (int e0 = 0; e0 < n; e0 += NT) {
-    const int e = e0 + threadIdx.x;
-    const int m = e < n ? merged[e] : -1;
-    int tot;
-    const int off = block_exclusive_scan<NT>(m >= 0 ? 1 : 0, tmp, &tot);
-    if (m >= 0) out[base + off] = m;
-    base += tot;
+  while (u) {
+    const int bit = __builtin_ctz(u);
+    u &= u - 1u;
+    const int owners = (int)((a >> bit) & 1u) | ((int)((b >> bit) & 1u) << 1);
+    out[off++] = (32 * w + bit) | (owners << 17);
   }
-  if (threadIdx.x == 0) tcount[item] = base;
+  if (threadIdx.x == 0) tcount[item] = tot;
 }
 
 // ---------------------------------------------------------------------------
