@@ -84,11 +84,13 @@ AttendWs attend_ws_layout(const Geo& g, int dtype, int max_parts) {
     L.vc = take((size_t)g.B * g.H * g.nb * g.Bt * g.d * 2);
     L.tlist = take((size_t)g.groups * tlist_cap(g) * sizeof(int));
     L.tcount = take((size_t)g.groups * sizeof(int));
+    L.icost = take((size_t)g.groups * sizeof(int));
   } else {
     L.kc = take(0);
     L.vc = take((size_t)g.B * g.N * g.H * g.d * sizeof(float));
     L.tlist = take(0);
     L.tcount = take(0);
+    L.icost = take(0);
   }
   L.part = take(split ? (size_t)max_parts * part_floats(g) * sizeof(float) : 0);
   L.total = off;

@@ -132,17 +132,18 @@ __device__ __forceinline__ int group_cost(const Geo& g, const int* row_ptr, int 
   return c;
 }
 
-// Key of queue entry r: a work item, or (split-and-merge) a work unit whose
+// Key of queue entry r: a work item (cost from the per-item table the bf16
+// prologue writes, else from the CSR), or (split-and-merge) a work unit whose
 // cost is the length of its range of the item's union list (at most 2nb).
-__device__ __forceinline__ unsigned sched_key(const Geo& g, const int* row_ptr, const int* units,
-                                              int r, int phased, int hpp) {
+__device__ __forceinline__ unsigned sched_key(const Geo& g, const int* row_ptr, const int* icost,
+                                              const int* units, int r, int phased, int hpp) {
   int item, cost;
   if (units) {
     item = units[4 * r];
     cost = units[4 * r + 2] - units[4 * r + 1];
   } else {
     item = r;
-    cost = group_cost(g, row_ptr, r);
+    cost = icost ? icost[r] : group_cost(g, row_ptr, r);
   }
   const unsigned k = (unsigned)(2 * g.nb - cost);
   return phased ? (unsigned)((item / g.groups_per_head) / hpp) * (unsigned)(2 * g.nb + 1) + k : k;
@@ -153,7 +154,8 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
                                                        int* __restrict__ buf_a,
                                                        int* __restrict__ buf_b,
                                                        int* __restrict__ counter,
-                                                       const int* __restrict__ units) {
+                                                       const int* __restrict__ units,
+                                                       const int* __restrict__ icost) {
   constexpr int NT = 512;
   __shared__ unsigned offs[16][NT];
   __shared__ unsigned stmp[NT / 64 + 1];
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
       for (int hh = threadIdx.x; hh < heads; hh += NT) hcost[hh] = 0;
       __syncthreads();
       for (int it = threadIdx.x; it < items; it += NT)
-        atomicAdd(&hcost[it / g.groups_per_head], group_cost(g, row_ptr, it));
+        atomicAdd(&hcost[it / g.groups_per_head], icost ? icost[it] : group_cost(g, row_ptr, it));
     }
     __syncthreads();
     // heads in (cost desc, index asc) order: each thread ranks its heads
@@ -250,7 +252,7 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
     for (int x = 0; x < 16; ++x) cnt[x] = 0u;
     for (int e = lo; e < hi; ++e) {
       const int r = src ? src[e] : e;
-      const unsigned dg = (sched_key(g, row_ptr, units, r, phased, hpp) >> sh) & 15u;
+      const unsigned dg = (sched_key(g, row_ptr, icost, units, r, phased, hpp) >> sh) & 15u;
 #pragma unroll
       for (int x = 0; x < 16; ++x) cnt[x] += (dg == (unsigned)x) ? 1u : 0u;
     }
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
     __syncthreads();
     for (int e = lo; e < hi; ++e) {
       const int r = src ? src[e] : e;
-      const unsigned dg = (sched_key(g, row_ptr, units, r, phased, hpp) >> sh) & 15u;
+      const unsigned dg = (sched_key(g, row_ptr, icost, units, r, phased, hpp) >> sh) & 15u;
       const unsigned pos = offs[dg][threadIdx.x]++;
       dst[pos] = r;
     }
@@ -298,7 +300,8 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
 __global__ __launch_bounds__(256) void tile_list_kernel(Geo g, const int* __restrict__ row_ptr,
                                                         const int* __restrict__ col_idx, int cap,
                                                         int* __restrict__ tlist,
-                                                        int* __restrict__ tcount) {
+                                                        int* __restrict__ tcount,
+                                                        int* __restrict__ icost) {
   constexpr int NT = 256, MAXW = MAX_NB / 32;
   static_assert(MAXW <= NT, "one bitmap word per thread");
   __shared__ uint32_t bA[MAXW], bB[MAXW];
@@ -339,7 +342,10 @@ __global__ __launch_bounds__(256) void tile_list_kernel(Geo g, const int* __rest
     const int owners = (int)((a >> bit) & 1u) | ((int)((b >> bit) & 1u) << 1);
     out[off++] = (32 * w + bit) | (owners << 17);
   }
-  if (threadIdx.x == 0) tcount[item] = tot;
+  if (threadIdx.x == 0) {
+    tcount[item] = tot;
+    icost[item] = nA + nB;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1065,10 +1071,12 @@ hipError_t launch_attend_schedule(const Geo& g, int dtype, const abs_mask* mask,
                                   hipStream_t s) {
   if (dtype == ABS_BF16)
     hipLaunchKernelGGL(tile_list_kernel, dim3(g.groups), dim3(256), 0, s, g, mask->row_ptr,
-                       mask->col_idx, tlist_cap(g), (int*)(ws + L.tlist), (int*)(ws + L.tcount));
+                       mask->col_idx, tlist_cap(g), (int*)(ws + L.tlist), (int*)(ws + L.tcount),
+                       (int*)(ws + L.icost));
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(512), 0, s, g, mask->row_ptr, sched,
                      heads_per_phase, (int*)(ws + L.sched), (int*)(ws + L.sort_a),
-                     (int*)(ws + L.sort_b), (int*)(ws + L.counter), (const int*)nullptr);
+                     (int*)(ws + L.sort_b), (int*)(ws + L.counter), (const int*)nullptr,
+                     dtype == ABS_BF16 ? (const int*)(ws + L.icost) : (const int*)nullptr);
   return hipGetLastError();
 }
 
@@ -1078,13 +1086,15 @@ hipError_t launch_attend_prepare_split(const Geo& g, const void* k, const void* 
                                        const AttendWs& L, hipStream_t s) {
   launch_relayout_bf16(g, k, v, ws, L, s);
   hipLaunchKernelGGL(tile_list_kernel, dim3(g.groups), dim3(256), 0, s, g, mask->row_ptr,
-                     mask->col_idx, tlist_cap(g), (int*)(ws + L.tlist), (int*)(ws + L.tcount));
+                     mask->col_idx, tlist_cap(g), (int*)(ws + L.tlist), (int*)(ws + L.tcount),
+                       (int*)(ws + L.icost));
   hipLaunchKernelGGL(split_units_kernel, dim3(1), dim3(1024), 0, s, g, (const int*)(ws + L.tcount),
                      split_tiles, max_parts, (int4*)(ws + L.units), (int4*)(ws + L.stab),
                      (int*)(ws + L.counter));
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(512), 0, s, g, mask->row_ptr, sched,
                      heads_per_phase, (int*)(ws + L.sched), (int*)(ws + L.sort_a),
-                     (int*)(ws + L.sort_b), (int*)(ws + L.counter), (const int*)(ws + L.units));
+                     (int*)(ws + L.sort_b), (int*)(ws + L.counter), (const int*)(ws + L.units),
+                     (const int*)(ws + L.icost));
   return hipGetLastError();
 }
 

@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256) void select_kernel(Geo g, float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// The same per-row selection with one wave per row (nb <= 512), no LDS sort
+// The same per-row selection with one wave per row (nb <= 2048), no LDS sort
 // and no workgroup barriers: element e = lane * KPL + r of the row lives in
 // register r of lane `lane`, and the bitonic network compares in registers for
 // strides below KPL and across lanes (shuffles) above.  Same keys, so the same
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256) void select_wave_kernel(Geo g, float* __restri
                                                           int* __restrict__ count, float p,
                                                           int k_floor, int write_prob) {
   constexpr int KPL = NBP / 64;   // keys per lane
-  static_assert(KPL >= 1 && KPL <= 8, "one wave per row up to 512 blocks");
+  static_assert(KPL >= 1 && KPL <= 32, "one wave per row up to 2048 blocks");
   __shared__ uint32_t bits[4][NBP / 32 > 1 ? NBP / 32 : 1];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + wv;
@@ -709,8 +709,8 @@ static void launch_select(const Geo& g, float* score, uint32_t* bm, int* cnt, fl
   else if (g.nb <= 128) launch_select_wave<128>(g, score, bm, cnt, p, kf, wp, s);
   else if (g.nb <= 256) launch_select_wave<256>(g, score, bm, cnt, p, kf, wp, s);
   else if (g.nb <= 512) launch_select_wave<512>(g, score, bm, cnt, p, kf, wp, s);
-  else if (g.nb <= 1024) launch_select_n<1024>(g, score, bm, cnt, p, kf, wp, s);
-  else if (g.nb <= 2048) launch_select_n<2048>(g, score, bm, cnt, p, kf, wp, s);
+  else if (g.nb <= 1024) launch_select_wave<1024>(g, score, bm, cnt, p, kf, wp, s);
+  else if (g.nb <= 2048) launch_select_wave<2048>(g, score, bm, cnt, p, kf, wp, s);
   else launch_select_n<4096>(g, score, bm, cnt, p, kf, wp, s);
 }
 
