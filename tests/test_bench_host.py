@@ -1,0 +1,58 @@
+"""Host-side logic of bench.py (CPU): the per-CU aggregation of telemetry
+records, the multi-GPU refusal, and the profile lookup."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def _hw(se, sa, cu):
+    return (se << 13) | (sa << 12) | (cu << 8)
+
+
+def test_cu_key_fields():
+    assert bench.cu_key(_hw(5, 1, 9), 3) == (3, 5, 1, 9)
+    assert bench.cu_key(_hw(0, 0, 0) | 0xff, 0x13) == (3, 0, 0, 0)   # low bits and high XCC bits ignored
+
+
+def test_imbalance_sums_workgroups_per_cu():
+    # two workgroups on one CU add up; max/mean over the three CUs
+    recs = np.array([
+        [_hw(0, 0, 1), 0, 10, 100],
+        [_hw(0, 0, 1), 0, 20, 50],     # same CU as the first
+        [_hw(0, 0, 2), 0, 15, 120],
+        [_hw(1, 0, 1), 1, 15, 180],
+    ])
+    r = bench.imbalance(recs)
+    assert r["cus"] == 3
+    tiles = np.array([30, 15, 15], float)
+    busy = np.array([150, 120, 180], float)
+    assert abs(r["tiles_max_over_mean"] - tiles.max() / tiles.mean()) < 1e-12
+    assert abs(r["busy_max_over_mean"] - busy.max() / busy.mean()) < 1e-12
+
+
+def test_balanced_records_give_one():
+    recs = np.array([[_hw(0, 0, c), x, 7, 70] for x in range(8) for c in range(4)])
+    r = bench.imbalance(recs)
+    assert r["cus"] == 32 and r["tiles_max_over_mean"] == 1.0 and r["busy_max_over_mean"] == 1.0
+
+
+def test_more_than_one_gpu_is_refused():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 2 and "one GPU" in p.stderr
+
+
+def test_traffic_profile_lookup():
+    # the committed profile gives a byte count for the workload and queue it was
+    # taken on, and nothing for another queue
+    t = bench.measured_traffic(1, "xcd_local")
+    assert t is None or t > 1e9
+    assert bench.measured_traffic(1, "head_major") is None
+    assert bench.measured_traffic(2, "xcd_local") is None
