@@ -114,13 +114,14 @@ __global__ __launch_bounds__(256) void kv_relayout_kernel(Geo g, const bf16_t* _
 
 // ---------------------------------------------------------------------------
 // Work schedule over attention work items (groups of one or two paired query
-// blocks of one head, see group_blocks).  A stable LSD radix sort (4-bit
-// digits, one workgroup) by key:
+// blocks of one head, see group_blocks), or over split-and-merge units.  A
+// stable LSD radix sort (4-bit digits, one workgroup) by key:
 //   NNZ_SORTED : key = 2nb - cost (largest first);
 //   HEAD_PHASED: key = phase * (2nb + 1) + 2nb - cost, phase = head / hpp;
-//   HEAD_MAJOR : natural order.
-// cost = kept blocks of the group's rows.  Ties keep item order.  Also resets
-// the persistent queue head.
+//   HEAD_MAJOR : natural order;
+//   XCD_LOCAL  : no sort; heads placed on XCDs, one queue per XCD (below).
+// cost = kept blocks of the group's rows (a unit: its number of union
+// entries).  Ties keep item order.  Also resets the persistent queue heads.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int group_cost(const Geo& g, const int* row_ptr, int item) {
   const int bh = item / g.groups_per_head, gl = item % g.groups_per_head;
@@ -475,7 +476,11 @@ __global__ void reset_counter_kernel(int* counter) {
 // K/V tiles are double buffered: the direct global->LDS copies of the next
 // union block (global_load_lds_dwordx4) run while the current one is
 // computed; one barrier per block.  PERSIST: workgroups pull work items from
-// an atomic queue (sched order) until it is exhausted.
+// an atomic queue (sched order; XCD-local: the queue of the XCD they run on,
+// then the others) until it is exhausted.  SPLIT: the queue holds work units,
+// each a range of an item's union list; a unit that is a part writes float32
+// partials (O^T before normalisation, its reference and its sum) to its slot
+// for merge_parts_kernel instead of the output.
 // ---------------------------------------------------------------------------
 template <int D, int BT>
 struct AttnCfg {
