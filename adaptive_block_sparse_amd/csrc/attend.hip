@@ -45,11 +45,35 @@ __host__ __device__ __forceinline__ int vt_perm(int k) {
 }
 
 // ---------------------------------------------------------------------------
+// Slot order inside a block tile: the block's real tokens come first, in
+// row-major (t, h, w) order over the block's real extent Tl x Hl x Wl, and the
+// padding slots follow.  For a whole block this is the row-major slot order of
+// the blocking; in a block cut by the grid edge it packs the real tokens, so
+// that whole 64-key chunks and 32-query subtiles of padding can be skipped.
+// Returns the token's offset ((st * Hg + sh) * W + sw) from the block's first
+// token, for slot s < Tl * Hl * Wl.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int packed_slot_offset(const Geo& g, int s, int Hl, int Wl) {
+  const int st = s / (Hl * Wl), r = s - st * (Hl * Wl);
+  const int sh = r / Wl, sw = r - sh * Wl;
+  return (st * g.Hg + sh) * g.W + sw;
+}
+
+// Real extent of block j: Tl | Hl << 8 | Wl << 16.
+__device__ __forceinline__ int block_extent(const Geo& g, int j) {
+  const int tb = j / (g.nbh * g.nbw), hb = (j / g.nbw) % g.nbh, wb = j % g.nbw;
+  const int Tl = min(g.bt, g.T - tb * g.bt), Hl = min(g.bh, g.Hg - hb * g.bh),
+            Wl = min(g.bw, g.W - wb * g.bw);
+  return Tl | (Hl << 8) | (Wl << 16);
+}
+
+// ---------------------------------------------------------------------------
 // K/V re-layout into the attention kernel's chunk-major block tiles (bf16):
 //   Kc[b, h, blk, c, key, 8]: 16-byte chunk c (d = 8c .. 8c+7) of every key;
 //   Vc[b, h, blk, c, d, 8]  : for every d, the 8 keys of key chunk c, in
 //                             vt_perm order;
-// zeros in padding slots.  A tile is then one contiguous BT*D*2-byte copy into
+// slots in the packed order above, zeros in padding slots.  A tile is then one
+// contiguous BT*D*2-byte copy into
 // LDS, and every MFMA operand read is (lane base + compile-time offset).  One
 // workgroup per (block, b*h, K|V).
 // ---------------------------------------------------------------------------
@@ -65,7 +89,8 @@ __global__ __launch_bounds__(256) void kv_relayout_kernel(Geo g, const bf16_t* _
   const int tb = blk / (g.nbh * g.nbw), hb = (blk / g.nbw) % g.nbh, wb = blk % g.nbw;
   const int Tl = min(g.bt, g.T - tb * g.bt), Hl = min(g.bh, g.Hg - hb * g.bh),
             Wl = min(g.bw, g.W - wb * g.bw);
-  const int plane = g.bh * g.bw;
+  const int nreal = Tl * Hl * Wl;
+  const long n0 = ((long)(tb * g.bt) * g.Hg + hb * g.bh) * g.W + wb * g.bw;
   const bf16_t* src = which == 0 ? k : v;
   // every load of this thread is issued before the first LDS store
   constexpr int NIT = (BT * (D / 8) + 255) / 256;
@@ -74,10 +99,9 @@ __global__ __launch_bounds__(256) void kv_relayout_kernel(Geo g, const bf16_t* _
   for (int it = 0; it < NIT; ++it) {
     const int e = threadIdx.x + 256 * it;
     const int s = e / (D / 8), c = e % (D / 8);
-    const int st = s / plane, sh = (s / g.bw) % g.bh, sw = s % g.bw;
     val[it] = make_uint4(0, 0, 0, 0);
-    if (e < BT * (D / 8) && st < Tl && sh < Hl && sw < Wl) {
-      const long n = ((long)(tb * g.bt + st) * g.Hg + hb * g.bh + sh) * g.W + wb * g.bw + sw;
+    if (e < BT * (D / 8) && s < nreal) {
+      const long n = n0 + packed_slot_offset(g, s, Hl, Wl);
       val[it] = *reinterpret_cast<const uint4*>(src + (((long)b * g.N + n) * g.H + h) * D + c * 8);
     }
   }
@@ -540,10 +564,8 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
   using C = AttnCfg<D, BT>;
   __shared__ __attribute__((aligned(1024))) char sK[2][C::TILE];
   __shared__ __attribute__((aligned(1024))) char sV[2][C::TILE];
-  __shared__ int s_off[BT];
-  __shared__ int s_crd[BT];
-  // per key block: real extent Tl | Hl << 8 | Wl << 16, partial << 24 (128-token
-  // blocks; smaller blocks run two workgroups per CU and keep their LDS)
+  // per key block: its number of real tokens (128-token blocks; smaller blocks
+  // run two workgroups per CU and keep their LDS)
   constexpr bool BINFO = BT == 128;
   __shared__ int s_binfo[BINFO ? MAX_NB : 1];
   __shared__ int s_item;
@@ -553,18 +575,14 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = w / C::NW1, wq = w % C::NW1;   // query block of the pair, wave in block
   const int hf = lane >> 5, l32 = lane & 31;
-  for (int s = tid; s < BT; s += C::NT) {
-    const int plane = g.bh * g.bw;
-    const int st = s / plane, sh = (s / g.bw) % g.bh, sw = s % g.bw;
-    s_off[s] = (st * g.Hg + sh) * g.W + sw;
-    s_crd[s] = st | (sh << 8) | (sw << 16);
-  }
+  // 32-query subtile of this wave.  Waves w and w + NW1 share a SIMD; with four
+  // subtiles per block the second block's waves take them rotated by two, so
+  // that when a cut block has only its first subtiles real, the busy waves of
+  // the pair sit on different SIMDs.
+  const int qsub = C::NW1 == 4 ? (wq + 2 * half) & 3 : wq;
   auto block_info = [&](int j) {
-    const int tb = j / (g.nbh * g.nbw), hb = (j / g.nbw) % g.nbh, wb = j % g.nbw;
-    const int Tl = min(g.bt, g.T - tb * g.bt), Hl = min(g.bh, g.Hg - hb * g.bh),
-              Wl = min(g.bw, g.W - wb * g.bw);
-    const int partial = (Tl < g.bt || Hl < g.bh || Wl < g.bw) ? 1 : 0;
-    return Tl | (Hl << 8) | (Wl << 16) | (partial << 24);
+    const int e = block_extent(g, j);
+    return (e & 255) * ((e >> 8) & 255) * ((e >> 16) & 255);   // real tokens
   };
   if constexpr (BINFO)
     for (int j = tid; j < g.nb; j += C::NT) s_binfo[j] = block_info(j);
@@ -660,15 +678,15 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
     int e2 = nt > 2 ? ld_scalar(tl, 2) : -1;
     if (e0 >= 0) issue(e0 & 0xffff, 0);
 
-    // this lane's query slot
+    // this lane's query slot (packed slot order, see packed_slot_offset)
     const int tq = iq / (g.nbh * g.nbw), hq = (iq / g.nbw) % g.nbh, wqb = iq % g.nbw;
     const int n0q = ((tq * g.bt) * g.Hg + hq * g.bh) * g.W + wqb * g.bw;
-    const int TlQ = g.T - tq * g.bt, HlQ = g.Hg - hq * g.bh, WlQ = g.W - wqb * g.bw;
-    const int qs = 32 * wq + l32;
-    const int qcrd = s_crd[qs];
-    const bool qvalid = active && (qcrd & 255) < TlQ && ((qcrd >> 8) & 255) < HlQ &&
-                        ((qcrd >> 16) & 255) < WlQ;
-    const long nq = n0q + s_off[qs];
+    const int extQ = block_extent(g, iq);
+    const int HlQ = (extQ >> 8) & 255, WlQ = (extQ >> 16) & 255;
+    const int nrealQ = (extQ & 255) * HlQ * WlQ;
+    const int qs = 32 * qsub + l32;
+    const bool qvalid = active && qs < nrealQ;
+    const long nq = n0q + (qvalid ? packed_slot_offset(g, qs, HlQ, WlQ) : 0);
     const bool wave_has_q = __any(qvalid);   // some real query in this wave's 32 slots
 
     // Q^T as the B operand: lane holds 8 consecutive d of query slot qs
@@ -709,16 +727,15 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
       if (jn >= 0) issue(jn, buf ^ 1);
 
       if (mine && wave_has_q) {
-        const int bi = __builtin_amdgcn_readfirstlane(BINFO ? s_binfo[j] : block_info(j));
-        const int Tl = bi & 255, Hl = (bi >> 8) & 255, Wl = (bi >> 16) & 255;
-        const bool partial = (bi >> 24) != 0;
+        const int nreal = __builtin_amdgcn_readfirstlane(BINFO ? s_binfo[j] : block_info(j));
+        const bool partial = nreal < BT;
         const char* kb = sK[buf] + kread;
         const char* vb = sV[buf] + vread;
 #pragma unroll
         for (int hc = 0; hc < C::NCH; ++hc) {
-          // a chunk whose first slot already lies beyond the block's last real
-          // frame holds only padding keys: nothing to add
-          if ((hc * C::CHS * 32) / (g.bh * g.bw) >= Tl) continue;
+          // a chunk whose first slot lies beyond the block's real tokens holds
+          // only padding keys: nothing to add
+          if (hc * C::CHS * 32 >= nreal) continue;
           // ---- S^T = K Q^T for the CHS key subtiles of this chunk
           f32x16_t s[C::CHS];
           // K operands read from LDS 4 products ahead of use (the order of the
@@ -746,9 +763,7 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
             }
             if (partial) {
               // padding keys: add -1e30 through one extra k-step (bias column x ones row)
-              const int crd = s_crd[32 * t + l32];
-              const bool ok =
-                  (crd & 255) < Tl && ((crd >> 8) & 255) < Hl && ((crd >> 16) & 255) < Wl;
+              const bool ok = 32 * t + l32 < nreal;
               bf16x8_t bias, ones;
 #pragma unroll
               for (int e = 0; e < 8; ++e) { bias[e] = (__bf16)0.0f; ones[e] = (__bf16)0.0f; }
@@ -893,12 +908,12 @@ __global__ __launch_bounds__(256) void merge_parts_kernel(Geo g, const int* __re
   const int half = qi / BT, qs = qi % BT;
   const int blk = half ? partner : lead;
   if (blk < 0) return;
-  const int plane = g.bh * g.bw;
   const int tb = blk / (g.nbh * g.nbw), hb = (blk / g.nbw) % g.nbh, wb = blk % g.nbw;
-  const int tt = tb * g.bt + qs / plane, hh = hb * g.bh + (qs / g.bw) % g.bh,
-            ww = wb * g.bw + qs % g.bw;
-  if (tt >= g.T || hh >= g.Hg || ww >= g.W) return;   // padding slot: no output
-  const long n = ((long)tt * g.Hg + hh) * g.W + ww;
+  const int ext = block_extent(g, blk);
+  const int Hl = (ext >> 8) & 255, Wl = (ext >> 16) & 255;
+  if (qs >= (ext & 255) * Hl * Wl) return;   // padding slot: no output
+  const long n = ((long)(tb * g.bt) * g.Hg + hb * g.bh) * g.W + wb * g.bw +
+                 packed_slot_offset(g, qs, Hl, Wl);
   const int b = bhh / g.H, h = bhh % g.H;
   const float* base = part + (long)slot0 * pf;
   const long mo = 2l * BT * D, lo = mo + 2 * BT;
