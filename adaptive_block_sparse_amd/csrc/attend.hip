@@ -59,6 +59,13 @@ __device__ __forceinline__ int packed_slot_offset(const Geo& g, int s, int Hl, i
   return (st * g.Hg + sh) * g.W + sw;
 }
 
+// Maximum of two scores.  The IEEE maximum (NaN propagating) needs no
+// quieting of its inputs, so chains of it become v_maximum3_f32; fmaxf would
+// first canonicalise every MFMA result.  Scores are finite.
+__device__ __forceinline__ float vmax(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 // Real extent of block j: Tl | Hl << 8 | Wl << 16.
 __device__ __forceinline__ int block_extent(const Geo& g, int j) {
   const int tb = j / (g.nbh * g.nbw), hb = (j / g.nbw) % g.nbh, wb = j % g.nbw;
@@ -316,7 +323,9 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
 // ---------------------------------------------------------------------------
 // Per attention work item (a pair of query blocks of one head, or a single
 // block), the union of its rows' kept key-block lists in ascending order, each
-// entry j | (kept by the first block) << 17 | (kept by the second) << 18.  One
+// entry j | (short) << 16 | (kept by the first block) << 17 | (kept by the
+// second) << 18, where short marks a key block whose real tokens all sit in the
+// first 64 slots of its tile (at most 64 real tokens, packed first).  One
 // workgroup per item: the two rows are marked in two LDS bitmaps of nb bits,
 // thread w takes word w of their union, and a workgroup scan of the words'
 // popcounts places each word's blocks, in ascending order, in the list.  The
@@ -365,7 +374,10 @@ __global__ __launch_bounds__(256) void tile_list_kernel(Geo g, const int* __rest
     const int bit = __builtin_ctz(u);
     u &= u - 1u;
     const int owners = (int)((a >> bit) & 1u) | ((int)((b >> bit) & 1u) << 1);
-    out[off++] = (32 * w + bit) | (owners << 17);
+    const int j = 32 * w + bit;
+    const int e = block_extent(g, j);
+    const int real = (e & 255) * ((e >> 8) & 255) * ((e >> 16) & 255);
+    out[off++] = j | ((real <= 64) << 16) | (owners << 17);
   }
   if (threadIdx.x == 0) {
     tcount[item] = tot;
@@ -655,16 +667,31 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
     const char* kc_head = (const char*)(a.kc + (long)bhh * g.nb * (D * BT));
     const char* vc_head = (const char*)(a.vc + (long)bhh * g.nb * (D * BT));
 
-    auto issue = [&](int jblk, int buf) {
+    // copies of the tile of union entry ent into buffer buf.  A short block
+    // (flag bit 16) has real tokens only in its first 64-key chunk, the only
+    // chunk the products read: the 1 KB copies that hold only keys of the second
+    // chunk are skipped.  In Kc a KB is 64 keys of one d chunk, so with 128-key
+    // tiles the odd waves copy only second-chunk keys; in Vc the second chunk
+    // starts at round V2 (a whole round, for D = 64 and 128).
+    auto issue = [&](int ent, int buf) {
+      const int jblk = ent & 0xffff;
+      constexpr bool SKIP = C::NCH == 2;   // 128-key tiles, two 64-key chunks
+      constexpr int V2 = SKIP ? 8 * (D * 16) / (C::NW * 1024) : C::ROUNDS;
+      static_assert(!SKIP || (BT * 16 == 2048 && (8 * D * 16) % (C::NW * 1024) == 0),
+                    "second-chunk copies: odd K waves and whole V rounds");
+      const bool short_blk = SKIP && ((ent >> 16) & 1) != 0;
       const char* ks = kc_head + (long)jblk * C::TILE;
       const char* vs = vc_head + (long)jblk * C::TILE;
+      if (!(short_blk && (w & 1))) {
 #pragma unroll
-      for (int rr = 0; rr < C::ROUNDS; ++rr) {
-        const int off = (rr * C::NW + w) * 1024;
-        dma16(ks + off + lane * 16, sK_base + buf * C::TILE + off);
+        for (int rr = 0; rr < C::ROUNDS; ++rr) {
+          const int off = (rr * C::NW + w) * 1024;
+          dma16(ks + off + lane * 16, sK_base + buf * C::TILE + off);
+        }
       }
 #pragma unroll
       for (int rr = 0; rr < C::ROUNDS; ++rr) {
+        if (rr >= V2 && short_blk) break;
         const int off = (rr * C::NW + w) * 1024;
         dma16(vs + off + lane * 16, sV_base + buf * C::TILE + off);
       }
@@ -676,7 +703,7 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
     int e0 = nt > 0 ? ld_scalar(tl, 0) : -1;
     int e1 = nt > 1 ? ld_scalar(tl, 1) : -1;
     int e2 = nt > 2 ? ld_scalar(tl, 2) : -1;
-    if (e0 >= 0) issue(e0 & 0xffff, 0);
+    if (e0 >= 0) issue(e0, 0);
 
     // this lane's query slot (packed slot order, see packed_slot_offset)
     const int tq = iq / (g.nbh * g.nbw), hq = (iq / g.nbw) % g.nbh, wqb = iq % g.nbw;
@@ -716,7 +743,7 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
     for (int t = 0; t < nt; ++t) {
       const int j = e0 & 0xffff;
       const bool mine = ((e0 >> (17 + half)) & 1) != 0;
-      const int jn = e1 >= 0 ? (e1 & 0xffff) : -1;
+      const int en = e1;
       if constexpr (SPLIT) tiles += ((e0 >> 17) & 1) + ((e0 >> 18) & 1);   // owned tiles
       e0 = e1;
       e1 = e2;
@@ -724,7 +751,7 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
 
       wait_vmcnt<0>();      // this thread's copies of block j have landed
       wg_barrier();         // ... everyone's; and block j-1's buffer is free
-      if (jn >= 0) issue(jn, buf ^ 1);
+      if (en >= 0) issue(en, buf ^ 1);
 
       if (mine && wave_has_q) {
         const int nreal = __builtin_amdgcn_readfirstlane(BINFO ? s_binfo[j] : block_info(j));
@@ -781,13 +808,13 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
 #pragma unroll
           for (int t2 = 0; t2 < C::CHS; ++t2)
 #pragma unroll
-            for (int e = (t2 == 0 ? 4 : 0); e < 16; ++e) mq[e & 3] = fmaxf(mq[e & 3], s[t2][e]);
-          float mt = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+            for (int e = (t2 == 0 ? 4 : 0); e < 16; ++e) mq[e & 3] = vmax(mq[e & 3], s[t2][e]);
+          float mt = vmax(vmax(mq[0], mq[1]), vmax(mq[2], mq[3]));
           {
             // the other half of the query column lives in lane l ^ 32
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt),
                                                              __float_as_uint(mt), false, false);
-            mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            mt = vmax(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
           }
           // lazily moved reference: only when the chunk maximum exceeds it by
           // more than 8 in the exp2 domain (probabilities stay <= 2^8)
@@ -796,13 +823,13 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
           const float alpha = up ? __builtin_amdgcn_exp2f((m_run - m_new) * a.c) : 1.0f;
           const float mc = m_new * a.c;
           bf16x8_t pop[2 * C::CHS];
-          float pq[4] = {0.f, 0.f, 0.f, 0.f};   // four independent partial sums
+          float pq[4];   // four independent partial sums
 #pragma unroll
           for (int t2 = 0; t2 < C::CHS; ++t2)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
               const float pv = __builtin_amdgcn_exp2f(fmaf(s[t2][e], a.c, -mc));
-              pq[e & 3] += pv;
+              pq[e & 3] = t2 == 0 && e < 4 ? pv : pq[e & 3] + pv;
               pop[2 * t2 + e / 8][e % 8] = (__bf16)pv;
             }
           const float psum = (pq[0] + pq[1]) + (pq[2] + pq[3]);
