@@ -326,9 +326,9 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
 // entry j | (short) << 16 | (kept by the first block) << 17 | (kept by the
 // second) << 18, where short marks a key block whose real tokens all sit in the
 // first 64 slots of its tile (at most 64 real tokens, packed first).  One
-// workgroup per item: the two rows are marked in two LDS bitmaps of nb bits,
-// thread w takes word w of their union, and a workgroup scan of the words'
-// popcounts places each word's blocks, in ascending order, in the list.  The
+// workgroup per item: the two rows are marked in two LDS bitmaps of nb bits, a
+// workgroup scan of the union's word popcounts gives each word's first list
+// position, and every kept block is written in ascending order from there.  The
 // list of item i starts at tlist[i * cap], cap = 2 nb, with tcount[i] entries.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void tile_list_kernel(Geo g, const int* __restrict__ row_ptr,
@@ -338,7 +338,8 @@ __global__ __launch_bounds__(256) void tile_list_kernel(Geo g, const int* __rest
                                                         int* __restrict__ icost) {
   constexpr int NT = 256, MAXW = MAX_NB / 32;
   static_assert(MAXW <= NT, "one bitmap word per thread");
-  __shared__ uint32_t bA[MAXW], bB[MAXW];
+  __shared__ uint32_t bA[MAXW], bB[MAXW], bS[MAXW];   // kept by A, by B; short blocks
+  __shared__ int woff[MAXW];                           // list position of each word's first
   __shared__ int tmp[NT / 64 + 1];
   const int item = blockIdx.x;
   const int bhh = item / g.groups_per_head, gl = item % g.groups_per_head;
@@ -353,8 +354,13 @@ __global__ __launch_bounds__(256) void tile_list_kernel(Geo g, const int* __rest
     nB = row_ptr[rB + 1] - pB;
   }
   const int W = (g.nb + 31) / 32;
-  for (int w = threadIdx.x; w < W; w += NT) { bA[w] = 0u; bB[w] = 0u; }
+  for (int w = threadIdx.x; w < W; w += NT) { bA[w] = 0u; bB[w] = 0u; bS[w] = 0u; }
   __syncthreads();
+  for (int j = threadIdx.x; j < g.nb; j += NT) {
+    const int e = block_extent(g, j);
+    if ((e & 255) * ((e >> 8) & 255) * ((e >> 16) & 255) <= 64)
+      atomicOr(&bS[j >> 5], 1u << (j & 31));
+  }
   for (int i = threadIdx.x; i < nA; i += NT) {
     const int v = col_idx[pA + i];
     atomicOr(&bA[v >> 5], 1u << (v & 31));
@@ -364,25 +370,27 @@ __global__ __launch_bounds__(256) void tile_list_kernel(Geo g, const int* __rest
     atomicOr(&bB[v >> 5], 1u << (v & 31));
   }
   __syncthreads();
-  const int w = threadIdx.x;
-  const uint32_t a = w < W ? bA[w] : 0u, b = w < W ? bB[w] : 0u;
-  uint32_t u = a | b;
-  int tot;
-  int off = block_exclusive_scan<NT>((int)__popc(u), tmp, &tot);
+  {
+    const int w = threadIdx.x;
+    const uint32_t u = w < W ? (bA[w] | bB[w]) : 0u;
+    int tot;
+    const int off = block_exclusive_scan<NT>((int)__popc(u), tmp, &tot);
+    if (w < W) woff[w] = off;
+    if (threadIdx.x == 0) tcount[item] = tot;
+  }
+  __syncthreads();
+  // every block of the union: its place is its word's offset plus the kept
+  // blocks below it in the word
   int* out = tlist + (long)item * cap;
-  while (u) {
-    const int bit = __builtin_ctz(u);
-    u &= u - 1u;
+  for (int j = threadIdx.x; j < g.nb; j += NT) {
+    const int wj = j >> 5, bit = j & 31;
+    const uint32_t a = bA[wj], b = bB[wj];
+    if (!(((a | b) >> bit) & 1u)) continue;
+    const int pos = woff[wj] + __popc((a | b) & ((1u << bit) - 1u));
     const int owners = (int)((a >> bit) & 1u) | ((int)((b >> bit) & 1u) << 1);
-    const int j = 32 * w + bit;
-    const int e = block_extent(g, j);
-    const int real = (e & 255) * ((e >> 8) & 255) * ((e >> 16) & 255);
-    out[off++] = j | ((real <= 64) << 16) | (owners << 17);
+    out[pos] = j | ((int)((bS[wj] >> bit) & 1u) << 16) | (owners << 17);
   }
-  if (threadIdx.x == 0) {
-    tcount[item] = tot;
-    icost[item] = nA + nB;
-  }
+  if (threadIdx.x == 0) icost[item] = nA + nB;
 }
 
 // ---------------------------------------------------------------------------
