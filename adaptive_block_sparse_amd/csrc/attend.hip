@@ -771,6 +771,10 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
           // a chunk whose first slot lies beyond the block's real tokens holds
           // only padding keys: nothing to add
           if (hc * C::CHS * 32 >= nreal) continue;
+          // only when the chunk's second subtile holds real keys are its score
+          // and PV products run (else its scores are the padding bias alone and
+          // its probabilities zero)
+          const bool two = C::CHS == 1 || (hc * C::CHS + 1) * 32 < nreal;
           // ---- S^T = K Q^T for the CHS key subtiles of this chunk
           f32x16_t s[C::CHS];
           // K operands read from LDS 4 products ahead of use (the order of the
@@ -786,25 +790,32 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
 #pragma unroll
           for (int t2 = 0; t2 < C::CHS; ++t2) {
             const int t = hc * C::CHS + t2;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) s[t2][e] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-              const int i = t2 * C::KS + ks;
-              const bf16x8_t av = kf[i % PDK];
-              if (i + PDK < NQ) kf[i % PDK] = *kaddr(i + PDK);
-              s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qop[ks], s[t2], 0, 0, 0);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-            if (partial) {
-              // padding keys: add -1e30 through one extra k-step (bias column x ones row)
+            // padding keys: add -1e30 through one extra k-step (bias column x ones row)
+            auto add_bias = [&](const f32x16_t& acc) {
               const bool ok = 32 * t + l32 < nreal;
               bf16x8_t bias, ones;
 #pragma unroll
               for (int e = 0; e < 8; ++e) { bias[e] = (__bf16)0.0f; ones[e] = (__bf16)0.0f; }
               if (hf == 0) ones[0] = (__bf16)1.0f;
               if (hf == 0 && !ok) bias[0] = (__bf16)(-1.0e30f);
-              s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias, ones, s[t2], 0, 0, 0);
+              return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias, ones, acc, 0, 0, 0);
+            };
+            f32x16_t zero;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) zero[e] = 0.f;
+            if (t2 == 0 || two) {
+              s[t2] = zero;
+#pragma unroll
+              for (int ks = 0; ks < C::KS; ++ks) {
+                const int i = t2 * C::KS + ks;
+                const bf16x8_t av = kf[i % PDK];
+                if (i + PDK < NQ) kf[i % PDK] = *kaddr(i + PDK);
+                s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qop[ks], s[t2], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+              if (partial) s[t2] = add_bias(s[t2]);
+            } else {
+              s[t2] = add_bias(zero);   // padding keys only: the scores are the bias alone
             }
           }
 
@@ -850,15 +861,20 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
           }
           m_run = m_new;
 
-          // ---- O^T += Vt P^T over the chunk's keys
+          // ---- O^T += Vt P^T over the chunk's keys, subtile by subtile (each
+          // o[u] still sums its 16-key steps in order)
 #pragma unroll
-          for (int u = 0; u < C::DSUB; ++u) {
+          for (int t2 = 0; t2 < C::CHS; ++t2) {
+            if (t2 > 0 && !two) break;
 #pragma unroll
-            for (int st2 = 0; st2 < 2 * C::CHS; ++st2) {
-              const int st = hc * 2 * C::CHS + st2;
-              const bf16x8_t av =
-                  *reinterpret_cast<const bf16x8_t*>(vb + st * (2 * D * 16) + u * 512);
-              o[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pop[st2], o[u], 0, 0, 0);
+            for (int u = 0; u < C::DSUB; ++u) {
+#pragma unroll
+              for (int st2 = 2 * t2; st2 < 2 * t2 + 2; ++st2) {
+                const int st = hc * 2 * C::CHS + st2;
+                const bf16x8_t av =
+                    *reinterpret_cast<const bf16x8_t*>(vb + st * (2 * D * 16) + u * 512);
+                o[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pop[st2], o[u], 0, 0, 0);
+              }
             }
           }
         }
