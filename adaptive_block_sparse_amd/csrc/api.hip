@@ -257,14 +257,11 @@ abs_status abs_attend_schedule(const abs_plan* plan, const abs_mask* mask, int32
 
 abs_status abs_attend_default_sched(const abs_plan* plan, int32_t* sched) {
   if (!plan_ok(plan) || !sched) return ABS_EINVAL;
-  // XCD-local keeps about one head per XCD in flight; that suits heads whose
-  // K and V, eight at a time, stay within about 192 MB of the 256 MB last-level
-  // cache.  Larger heads go through the head-phased queue, whose phases are
-  // sized to fit.
-  const double per_head = 2.0 * (double)plan->tokens * plan->s.head_dim *
-                          (plan->s.dtype == ABS_BF16 ? 2 : 4);
-  *sched = (plan->s.dtype == ABS_BF16 && NXCD * per_head <= 192.0e6) ? ABS_SCHED_XCD_LOCAL
-                                                                      : ABS_SCHED_HEAD_PHASED;
+  // With phases of about 48 MB of K and V (a few heads at 480p, one at 720p
+  // and on the 81-frame shape), the head-phased queue measured fastest on every
+  // workload: 0.5 % ahead of XCD-local at 480p, 1-2 % on the head-imbalance
+  // stress, 5-6 % at 720p and on the 81-frame shape.
+  *sched = ABS_SCHED_HEAD_PHASED;
   return ABS_OK;
 }
 

@@ -146,9 +146,10 @@ __global__ __launch_bounds__(256) void kv_relayout_kernel(Geo g, const bf16_t* _
 // ---------------------------------------------------------------------------
 // Work schedule over attention work items (groups of one or two paired query
 // blocks of one head, see group_blocks), or over split-and-merge units.  A
-// stable LSD radix sort (4-bit digits, one workgroup) by key:
+// stable LSD radix sort (4-bit digits, one workgroup per sorted range) by key:
 //   NNZ_SORTED : key = 2nb - cost (largest first);
-//   HEAD_PHASED: key = phase * (2nb + 1) + 2nb - cost, phase = head / hpp;
+//   HEAD_PHASED: key = phase * (2nb + 1) + 2nb - cost, phase = head / hpp
+//                (work items: each phase's range sorted by its own workgroup);
 //   HEAD_MAJOR : natural order;
 //   XCD_LOCAL  : no sort; heads placed on XCDs, one queue per XCD (below).
 // cost = kept blocks of the group's rows (a unit: its number of union
@@ -193,8 +194,10 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
   __shared__ unsigned stmp[NT / 64 + 1];
   // queue entries: work items, or the split units counted by split_units_kernel
   const int items = units ? counter[NUNITS] : g.groups;
-  if (threadIdx.x == 0) counter[0] = 0;
-  if (threadIdx.x < NXCD) counter[QHEAD + 32 * threadIdx.x] = 0;
+  if (blockIdx.x == 0) {
+    if (threadIdx.x == 0) counter[0] = 0;
+    if (threadIdx.x < NXCD) counter[QHEAD + 32 * threadIdx.x] = 0;
+  }
   if (mode == ABS_SCHED_HEAD_MAJOR) {
     for (int r = threadIdx.x; r < items; r += NT) sched[r] = r;
     return;
@@ -268,13 +271,23 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
     }
     return;
   }
-  const int phased = mode == ABS_SCHED_HEAD_PHASED;
+  // Work items (not split units) sit head by head, so under HEAD_PHASED each
+  // phase is a contiguous range of them and the queue is that range sorted by
+  // cost alone: one workgroup per phase (the launch's grid) sorts its range.
+  int phased = mode == ABS_SCHED_HEAD_PHASED;
+  int base = 0, n = items;
+  if (phased && !units) {
+    base = blockIdx.x * hpp * g.groups_per_head;
+    n = min(items - base, hpp * g.groups_per_head);
+    phased = 0;
+    if (n <= 0) return;
+  }
   const int nphase = phased ? (g.B * g.H + hpp - 1) / hpp : 1;
   const unsigned maxkey = (unsigned)nphase * (unsigned)(2 * g.nb + 1);
   int passes = 1;
   while (passes < 8 && (maxkey >> (4 * passes)) != 0u) ++passes;
-  const int per = (items + NT - 1) / NT;
-  const int lo = threadIdx.x * per, hi = min(items, lo + per);
+  const int per = (n + NT - 1) / NT;
+  const int lo = base + threadIdx.x * per, hi = min(base + n, lo + per);
   for (int pass = 0; pass < passes; ++pass) {
     const int* src = pass == 0 ? nullptr : ((pass & 1) ? buf_a : buf_b);
     int* dst = pass == passes - 1 ? sched : ((pass & 1) ? buf_b : buf_a);
@@ -313,7 +326,7 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
       const int r = src ? src[e] : e;
       const unsigned dg = (sched_key(g, row_ptr, icost, units, r, phased, hpp) >> sh) & 15u;
       const unsigned pos = offs[dg][threadIdx.x]++;
-      dst[pos] = r;
+      dst[base + pos] = r;
     }
     __syncthreads();
   }
@@ -1144,7 +1157,10 @@ hipError_t launch_attend_schedule(const Geo& g, int dtype, const abs_mask* mask,
     hipLaunchKernelGGL(tile_list_kernel, dim3(g.groups), dim3(256), 0, s, g, mask->row_ptr,
                        mask->col_idx, tlist_cap(g), (int*)(ws + L.tlist), (int*)(ws + L.tcount),
                        (int*)(ws + L.icost));
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(512), 0, s, g, mask->row_ptr, sched,
+  // head-phased work items: one workgroup per phase
+  const int grid = sched == ABS_SCHED_HEAD_PHASED
+                       ? (g.B * g.H + heads_per_phase - 1) / heads_per_phase : 1;
+  hipLaunchKernelGGL(schedule_kernel, dim3(grid), dim3(512), 0, s, g, mask->row_ptr, sched,
                      heads_per_phase, (int*)(ws + L.sched), (int*)(ws + L.sort_a),
                      (int*)(ws + L.sort_b), (int*)(ws + L.counter), (const int*)nullptr,
                      dtype == ABS_BF16 ? (const int*)(ws + L.icost) : (const int*)nullptr);

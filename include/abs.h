@@ -227,11 +227,12 @@ abs_status abs_attend(const abs_plan* plan, const void* q, const void* k, const 
                       const abs_mask* mask, void* o, int32_t sched, void* ws,
                       size_t ws_bytes, int64_t* telemetry, void* stream);
 
-/* The schedule that measured fastest for this plan's shape on MI355X: XCD_LOCAL
- * when the K and V of eight heads (one per XCD) take at most 192 MB, else
- * HEAD_PHASED, whose phases keep the heads in flight inside the last-level
- * cache (480p: XCD_LOCAL; 720p and the 81-frame 1.3B shape: HEAD_PHASED, 4-6 %
- * faster there).  Host query. */
+/* The schedule that measured fastest for this plan's shape on MI355X.  With
+ * phases that keep about 48 MB of K and V in flight, HEAD_PHASED led on every
+ * workload measured (480p by 0.5 % over XCD_LOCAL, the head-imbalance stress
+ * by 1-2 %, 720p and the 81-frame 1.3B shape by 5-6 %), so it is returned for
+ * every plan; the query stays so that callers need not hard-code it.  Host
+ * query. */
 abs_status abs_attend_default_sched(const abs_plan* plan, int32_t* sched);
 
 /* Number of workgroups abs_attend_run launches for this plan and schedule on

@@ -51,8 +51,11 @@ def test_more_than_one_gpu_is_refused():
 
 def test_traffic_profile_lookup():
     # the committed profile gives a byte count for the workload and queue it was
-    # taken on, and nothing for another queue
-    t = bench.measured_traffic(1, "xcd_local")
+    # taken on (while the kernel source is unchanged), and nothing for another
+    # queue or workload
+    path = os.path.join(ROOT, "profiles", "attn_bf16_wan22_480p_hbm_traffic.md")
+    sched = next(l.split(":", 1)[1].strip() for l in open(path) if l.startswith("sched:"))
+    t = bench.measured_traffic(1, sched)
     assert t is None or t > 1e9
     assert bench.measured_traffic(1, "head_major") is None
-    assert bench.measured_traffic(2, "xcd_local") is None
+    assert bench.measured_traffic(2, sched) is None

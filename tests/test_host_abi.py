@@ -227,7 +227,7 @@ def test_relayout_and_schedule_validation():
                                    None) == A.ENOSPACE
 
 
-@pytest.mark.parametrize("cfg,want", [(1, A.SCHED_XCD_LOCAL), (3, A.SCHED_XCD_LOCAL),
+@pytest.mark.parametrize("cfg,want", [(1, A.SCHED_HEAD_PHASED), (3, A.SCHED_HEAD_PHASED),
                                       (2, A.SCHED_HEAD_PHASED), (4, A.SCHED_HEAD_PHASED),
                                       (0, A.SCHED_HEAD_PHASED)])
 def test_default_sched(cfg, want):
