@@ -30,7 +30,9 @@
  * (bt, bh, bw) blocks.  Block index ((t/bt)*nbh + h/bh)*nbw + w/bw and slot
  * ((t%bt)*bh + h%bh)*bw + w%bw are row-major at both levels; query and key
  * blocks share this blocking.  Padding tokens do not exist: they are excluded
- * from the pooled means, masked as keys and produce no output.
+ * from the pooled means, masked as keys and produce no output.  (Inside the
+ * attention workspace a cut block's tile stores its real tokens first; that
+ * order is internal and changes nothing above.)
  *
  * Errors.  Every entry point validates its arguments on the host before any
  * launch and returns ABS_EINVAL / ABS_ENOTSUP / ABS_ENOSPACE without touching
@@ -255,8 +257,9 @@ abs_status abs_attend_grid(const abs_plan* plan, int32_t sched, int32_t* workgro
  * [p*nt/P, (p+1)*nt/P) (integer division).  Items are cut heaviest first (nt
  * descending, ties by lower item index) while the running sum of their P stays
  * within max_parts; the first that does not fit ends the cutting, and the rest
- * stay whole.  Slots are numbered over the cut items in item order.  Each part writes float32 partials (O not yet
- * normalised, its reference maximum and its sum, per query); a merge kernel
+ * stay whole.  Slots are numbered over the cut items in item order.  Each
+ * part writes float32 partials (O not yet normalised, its reference maximum
+ * and its sum, per query); a merge kernel
  * then writes o for the cut items.  The result is the same softmax up to
  * rounding (parts' partials are float32, combined in ascending part order), is
  * bitwise independent of the queue order, and equals abs_attend_run's output
