@@ -509,8 +509,9 @@ __global__ void reset_counter_kernel(int* counter) {
 // ---------------------------------------------------------------------------
 // bf16 block-sparse attention.  A workgroup handles one work item: a pair of
 // neighbouring query blocks of one head (or a single block), 4 waves per
-// query block (BT = 128), wave w owning query slots 32*(w%NW1) .. +31 of block
-// w/NW1.  The workgroup walks the union of the two ascending kept-block lists
+// query block (BT = 128), wave w owning one 32-query subtile of block w/NW1
+// (subtile w%NW1, rotated by two in the second block).  The workgroup walks
+// the union of the two ascending kept-block lists
 // (precomputed per item by tile_list_kernel and read two entries ahead);
 // each K/V tile is copied into LDS once and serves both blocks, which halves
 // the K/V traffic per flop (neighbouring blocks keep nearly the same key
@@ -519,7 +520,10 @@ __global__ void reset_counter_kernel(int* counter) {
 //   S^T (keys x queries) = K_j Q^T with v_mfma_f32_32x32x16_bf16 (Q^T held in
 //     registers as the B operand, K_j read from LDS as the A operand);
 //   padding keys get -1e30 through one extra MFMA k-step (bias column times a
-//     ones row), so no per-element masking is needed;
+//     ones row), so no per-element masking is needed; a cut block's real
+//     tokens come first in its tile, so chunks and 32-key subtiles of padding
+//     keys, and waves of padding queries, skip their products (and a short
+//     block the copies of its second chunk);
 //   online softmax per query column: running sum in float32, exp2 with
 //     log2(e)/sqrt(d) folded into one FMA, and a lazily moved reference: a
 //     lane's reference moves to the chunk maximum only when that maximum

@@ -46,11 +46,22 @@ def imbalance(tel: np.ndarray):
                 busy_max_over_mean=float(b.max() / b.mean()))
 
 
+def code_digest(path: str) -> str:
+    """sha256 of a C++/HIP source with its comments and blank space removed:
+    it changes when the code changes, not when only a comment does."""
+    import hashlib
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
 def measured_traffic(workload_cfg: int, sched: str):
     """HBM bytes per launch of the attention kernel from the committed rocprofv3
     FETCH_SIZE/WRITE_SIZE summary, if it was taken on this workload and launch
-    and the kernel source has not changed since (else None)."""
-    import hashlib
+    and the kernel code has not changed since (else None)."""
     path = os.path.join(ROOT, "profiles", "attn_bf16_wan22_480p_hbm_traffic.md")
     src = os.path.join(ROOT, "adaptive_block_sparse_amd", "csrc", "attend.hip")
     if workload_cfg != 1 or not os.path.exists(path):
@@ -60,8 +71,7 @@ def measured_traffic(workload_cfg: int, sched: str):
         if ":" in line and not line.startswith((" ", "|", "#")):
             key, _, val = line.partition(":")
             fields[key.strip()] = val.strip()
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if (fields.get("attend_hip_sha256") != sha or fields.get("sched") != sched
+    if (fields.get("attend_hip_code_sha256") != code_digest(src) or fields.get("sched") != sched
             or "traffic_bytes_per_launch" not in fields):
         return None
     return int(fields["traffic_bytes_per_launch"])

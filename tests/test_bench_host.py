@@ -59,3 +59,15 @@ def test_traffic_profile_lookup():
     assert t is None or t > 1e9
     assert bench.measured_traffic(1, "head_major") is None
     assert bench.measured_traffic(2, sched) is None
+
+
+def test_code_digest_ignores_comments_only(tmp_path):
+    # the profile match survives comment edits and fails on any code edit
+    a = tmp_path / "a.hip"
+    a.write_text("// header\nint f(int x) {  /* note */\n  return x + 1;   // one\n}\n")
+    b = tmp_path / "b.hip"
+    b.write_text("/* other\n   header */\nint f(int x) {\n\n  return x + 1;\n}\n")
+    c = tmp_path / "c.hip"
+    c.write_text("// header\nint f(int x) {  /* note */\n  return x + 2;   // one\n}\n")
+    assert bench.code_digest(str(a)) == bench.code_digest(str(b))
+    assert bench.code_digest(str(a)) != bench.code_digest(str(c))
