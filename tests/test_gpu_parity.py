@@ -45,6 +45,12 @@ SMALL = {
     "bf16-pair-w-odd": _wl(109, (2, 8, 40), (2, 8, 8), 2, 128, "bf16"),    # nbt = nbh = 1, nbw = 5
     "bf16-d64-bt128": _wl(110, (5, 12, 20), (2, 8, 8), 2, 64, "bf16"),
     "bf16-block-4x4x4": _wl(111, (9, 10, 11), (4, 4, 4), 2, 128, "bf16"),
+    # 128-token blocks of other shapes, cut on every axis: real counts 128, 96,
+    # 80, 64, 60, 48, 40, 30 (and 128, 80, 40, 25), so whole padding chunks,
+    # padding-only second subtiles, short-block copies and packed slots of
+    # several extents all occur
+    "bf16-block-4x4x8": _wl(114, (7, 10, 13), (4, 4, 8), 3, 128, "bf16"),
+    "bf16-block-1x8x16": _wl(115, (3, 13, 21), (1, 8, 16), 2, 128, "bf16"),
     "f32-d64-bt128": _wl(112, (3, 9, 10), (2, 8, 8), 2, 64, "f32"),
 }
 
@@ -95,7 +101,7 @@ def test_small_full_parity(name):
         assert np.array_equal(o2, r["o"])
 
 
-@pytest.mark.parametrize("name", ["bf16-d128-bt128-ragged", "f32-tiny-cfg0"])
+@pytest.mark.parametrize("name", ["bf16-d128-bt128-ragged", "f32-tiny-cfg0", "bf16-block-4x4x8"])
 def test_dense_when_p_is_one(name):
     wl = SMALL[name]
     r = _run(wl, 1.0, 1)
