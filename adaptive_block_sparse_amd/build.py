@@ -14,21 +14,25 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libabs.so")
 SOURCES = ["api.hip", "route.hip", "attend.hip"]
+# measurement aid (sustained MFMA rate and clock), a library of its own
+PROBE_LIB = os.path.join(HERE, "libabs_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 ARCH = os.environ.get("ABS_OFFLOAD_ARCH", "gfx950")
 
 
-def hipcc_command(out: str = LIB):
+def hipcc_command(out: str = LIB, sources=None):
+    sources = SOURCES if sources is None else sources
     return ["/opt/rocm/bin/hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             "-shared", "-Wall", "-Wno-unused-function",
             # no packed-fp32 instructions anywhere in the device code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
+            *[os.path.join(CSRC, s) for s in sources], "-o", out]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = hipcc_command(tmp)
+def _compile(lib: str, sources, verbose: bool) -> str:
+    tmp = lib + ".tmp"
+    cmd = hipcc_command(tmp, sources)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -38,8 +42,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    _compile(PROBE_LIB, PROBE_SOURCES, verbose)
+    return _compile(LIB, SOURCES, verbose)
 
 
 if __name__ == "__main__":

@@ -86,6 +86,50 @@ def block_valid_counts(grid, block) -> np.ndarray:
     return np.einsum("i,j,k->ijk", *per_axis).ravel()
 
 
+def mfma_probe(dev, iters: int = 40000, workgroups: int = 1024, launches: int = 5):
+    """Sustained bf16 MFMA rate of this GPU on its own (libabs_probe.so, a
+    measurement aid): every SIMD issues v_mfma_f32_32x32x16_bf16 back to back
+    on varied operands.  Median of `launches` timed launches after two untimed
+    ones.  clock64_ghz is the rate of the device's clock64 counter against its
+    wall clock during the product loops."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "adaptive_block_sparse_amd", "libabs_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (python -m adaptive_block_sparse_amd.build)")
+    lib = ctypes.CDLL(path)
+    lib.abs_probe_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+    lib.abs_probe_wall_clock_khz.argtypes = [ctypes.POINTER(ctypes.c_int32)]
+    out = torch.empty(workgroups * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(workgroups * 2, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    khz = ctypes.c_int32(0)
+    if lib.abs_probe_wall_clock_khz(ctypes.byref(khz)) != 0 or khz.value <= 0:
+        raise RuntimeError("wall clock rate query failed")
+    times, clk = [], []
+    for i in range(2 + launches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = lib.abs_probe_mfma_bf16(iters, workgroups, ctypes.c_void_p(out.data_ptr()),
+                                     ctypes.c_void_p(clocks.data_ptr()),
+                                     ctypes.c_void_p(stream.cuda_stream))
+        e1.record(stream)
+        if rc != 0:
+            raise RuntimeError(f"abs_probe_mfma_bf16 returned {rc}")
+        torch.cuda.synchronize()
+        if i >= 2:
+            times.append(e0.elapsed_time(e1) * 1e-3)
+            c = clocks.cpu().numpy().reshape(-1, 2).astype(np.float64)
+            clk.append(float(np.median(c[:, 0] / (c[:, 1] / (khz.value * 1e3)))) / 1e9)
+    assert bool(torch.isfinite(out).all())
+    flop = workgroups * 4 * iters * 4 * 32 * 32 * 16 * 2
+    t = float(np.median(times))
+    return {"tflops": round(flop / t / 1e12, 1), "clock64_ghz": round(float(np.median(clk)), 3),
+            "ms_per_launch": round(t * 1e3, 3), "iters": iters, "workgroups": workgroups,
+            "launches": launches}
+
+
 def cpu_baseline(wl, p, inputs, rp, ci, budget_s=20.0):
     """The oracle, as it stands, on the host cores: full routing of every row,
     attention on a seeded row sample extrapolated by kept tiles."""
@@ -155,6 +199,11 @@ def main():
                          "configuration, as profiler summaries need")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for HBM counter scaling)")
+    ap.add_argument("--mfma-peak", action="store_true",
+                    help="run only the MFMA probe: the bf16 rate this GPU sustains on its own "
+                         "and its shader clock meanwhile")
+    ap.add_argument("--probe-launches", type=int, default=5,
+                    help="timed launches of the MFMA probe (about 14 ms each)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -175,6 +224,9 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": 1 << 30, "launches": 3}))
+        return
+    if args.mfma_peak:
+        print(json.dumps({"mfma_probe_bf16": mfma_probe(dev, launches=args.probe_launches)}))
         return
 
     import adaptive_block_sparse_amd as A
@@ -398,6 +450,10 @@ def main():
                  "tflops": round(4.0 * bt * bt * d * dense_tiles / (dense_ms * 1e-3) / 1e12, 2),
                  "speedup_sparse_over_dense": round(dense_ms / t_attn, 3)}
 
+    # the bf16 MFMA rate this GPU sustains on its own (power-limited clock),
+    # reported beside the data-sheet peak
+    probe = mfma_probe(dev) if (not args.timed_only and wl.dtype == "bf16") else None
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -442,7 +498,9 @@ def main():
                                 "attn_bf16_kernel<128,128,false,false>"
                                 if args.sched == "head_major"
                                 else "attn_bf16_kernel<128,128,true,false>"),
-                     "per_unit": "4*Bt^2*d flop per kept tile"},
+                     "per_unit": "4*Bt^2*d flop per kept tile",
+                     "probe_peak": probe["tflops"] if probe else None},
+        "mfma_probe_bf16": probe,
         "route_hbm": {"bytes_read_qk": 2 * wl.tokens * wl.heads * wl.head_dim * 2,
                       "gbs_algorithmic": round(2 * wl.tokens * wl.heads * wl.head_dim * 2
                                                / (t_route * 1e-3) / 1e9, 1)},

@@ -370,3 +370,13 @@ def test_relayout_beside_routing_on_a_second_stream():
         A.attend_run(plan, q, k, mask, o, A.SCHED_XCD_LOCAL, ws)
         torch.cuda.synchronize()
         assert np.array_equal(o.float().cpu().numpy(), want)
+
+
+def test_mfma_probe_runs():
+    """The measurement aid: a short probe launch gives finite sums, a positive
+    rate and a clock64 rate inside the chip's range."""
+    import bench
+    r = bench.mfma_probe(DEV, iters=200, workgroups=256, launches=2)
+    print("probe", r)
+    assert r["tflops"] > 0
+    assert 0.5 < r["clock64_ghz"] < 3.0

@@ -31,6 +31,27 @@ def test_exports_match_header():
     assert A.status_string(A.ENOSPACE) == "workspace too small"
 
 
+def test_probe_library_exports_its_header():
+    # the measurement aid (sustained MFMA rate) is a library of its own
+    path = os.path.join(ROOT, "adaptive_block_sparse_amd", "libabs_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libabs_probe.so not built")
+    lib = ctypes.CDLL(path)
+    header = open(os.path.join(ROOT, "include", "abs_probe.h")).read()
+    declared = set(re.findall(r"^\s*int\s+(abs_probe_\w+)\s*\(", header, re.M))
+    assert declared == {"abs_probe_mfma_bf16", "abs_probe_wall_clock_khz"}
+    for name in declared:
+        assert hasattr(lib, name)
+    f = lib.abs_probe_mfma_bf16
+    f.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    # invalid arguments are rejected before any launch
+    assert f(0, 4, FAKE, FAKE, None) == 1
+    assert f(10, 0, FAKE, FAKE, None) == 1
+    assert f(10, 4, None, FAKE, None) == 1
+    assert lib.abs_probe_wall_clock_khz(None) == 1
+
+
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 def test_plan_matches_geometry(cfg):
     _lib()
