@@ -635,28 +635,33 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
 
   // queue length: work items, or the split units (written by the prologue)
   const int qlen = SPLIT ? ld_scalar(a.counter, NUNITS) : g.groups;
+  // claim of a queue position (thread 0 only); past the end: >= qlen
+  auto pull = [&]() {
+    if (a.xcd_local) {
+      // own XCD's queue first, then steal from the others in turn
+      const int x0 = (int)(xcc_id_reg() & (NXCD - 1));
+      int found = g.groups;
+      for (int k = 0; k < NXCD; ++k) {
+        const int x = (x0 + k) & (NXCD - 1);
+        const int q0 = a.counter[QOFF + x], q1 = a.counter[QOFF + x + 1];
+        if (q0 == q1) continue;
+        const int idx = atomicAdd(&a.counter[QHEAD + 32 * x], 1);
+        if (q0 + idx < q1) { found = q0 + idx; break; }
+      }
+      return found;
+    }
+    return atomicAdd(a.counter, 1);
+  };
+  // the next position is claimed before the previous item's output stores, so
+  // that its round trip overlaps them, and the workgroup meets at a barrier
+  // that waits for LDS only: those stores stay in flight into the next item
+  int claimed = 0;
   int iter = 0;
   while (true) {
     int item;
     if (PERSIST) {
-      if (tid == 0) {
-        if (a.xcd_local) {
-          // own XCD's queue first, then steal from the others in turn
-          const int x0 = (int)(xcc_id_reg() & (NXCD - 1));
-          int found = g.groups;
-          for (int k = 0; k < NXCD; ++k) {
-            const int x = (x0 + k) & (NXCD - 1);
-            const int q0 = a.counter[QOFF + x], q1 = a.counter[QOFF + x + 1];
-            if (q0 == q1) continue;
-            const int idx = atomicAdd(&a.counter[QHEAD + 32 * x], 1);
-            if (q0 + idx < q1) { found = q0 + idx; break; }
-          }
-          s_item = found;
-        } else {
-          s_item = atomicAdd(a.counter, 1);
-        }
-      }
-      __syncthreads();
+      if (tid == 0) s_item = iter == 0 ? pull() : claimed;
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       item = __builtin_amdgcn_readfirstlane(s_item);
       if (item >= qlen) break;
       item = ld_scalar(a.sched, item);
@@ -899,6 +904,7 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
       buf ^= 1;
     }
     if constexpr (!SPLIT) tiles += nA + nB;
+    if (PERSIST && tid == 0) claimed = pull();
 
     // ---- epilogue: normalise and store the real query rows
     const float l_tot = l_run + __shfl_xor(l_run, 32);
