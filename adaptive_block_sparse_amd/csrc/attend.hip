@@ -785,7 +785,6 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
 
       if (mine && wave_has_q) {
         const int nreal = __builtin_amdgcn_readfirstlane(BINFO ? s_binfo[j] : block_info(j));
-        const bool partial = nreal < BT;
         const char* kb = sK[buf] + kread;
         const char* vb = sV[buf] + vread;
 #pragma unroll
@@ -835,7 +834,9 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
                 s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qop[ks], s[t2], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
               }
-              if (partial) s[t2] = add_bias(s[t2]);
+              // only the subtile that holds the block's last real key also
+              // holds padding keys
+              if (32 * (t + 1) > nreal) s[t2] = add_bias(s[t2]);
             } else {
               s[t2] = add_bias(zero);   // padding keys only: the scores are the bias alone
             }
