@@ -29,19 +29,9 @@ Geo make_geo(const abs_plan* plan) {
   g.N = (int)plan->tokens;
   g.rows = (int)plan->rows;
   g.words = (g.nb + 31) / 32;
-  // pair along t (closest kept sets), else h, else w
-  if (g.nbt >= 2) {
-    g.pair_axis = 0; g.pair_stride = g.nbh * g.nbw;
-    g.groups_per_head = ((g.nbt + 1) / 2) * g.nbh * g.nbw;
-  } else if (g.nbh >= 2) {
-    g.pair_axis = 1; g.pair_stride = g.nbw;
-    g.groups_per_head = g.nbt * ((g.nbh + 1) / 2) * g.nbw;
-  } else if (g.nbw >= 2) {
-    g.pair_axis = 2; g.pair_stride = 1;
-    g.groups_per_head = g.nbt * g.nbh * ((g.nbw + 1) / 2);
-  } else {
-    g.pair_axis = -1; g.pair_stride = 0; g.groups_per_head = g.nb;
-  }
+  // pair along t (closest kept sets), the left-over plane along h, its
+  // left-over row along w
+  g.groups_per_head = groups_per_head_of(g.nbt, g.nbh, g.nbw);
   g.groups = g.B * g.H * g.groups_per_head;
   return g;
 }

@@ -18,31 +18,54 @@ struct Geo {
   int N;               // tokens
   int rows;            // B*H*nb
   int words;           // 32-bit words of one row bitmap, ceil(nb/32)
-  // Attention work items pair two query blocks that are neighbours along one
-  // block axis (they share most kept key blocks, so one K/V tile serves both).
-  int pair_axis;       // 0 = t, 1 = h, 2 = w, -1 = no pairing (nb == 1)
-  int pair_stride;     // block-index distance to the partner
+  // Attention work items pair two query blocks that are neighbours (they keep
+  // most of the same key blocks, so one K/V tile copy serves both): along t,
+  // then in a left-over last t-plane along h, then in a left-over last h-row of
+  // that plane along w; a block left over after that stands alone.
   int groups_per_head; // work items per head
   int groups;          // B*H*groups_per_head
 };
 
-// Leader block and partner (or -1) of group gl of a head.
+// Work items of one head, in this order:
+//   (nbt/2) * nbh * nbw  t-pairs    (2tp, h, w) + (2tp+1, h, w);
+//   if nbt is odd, in plane t = nbt-1:
+//     (nbh/2) * nbw      h-pairs    (t, 2hp, w) + (t, 2hp+1, w);
+//     if nbh is odd, in row h = nbh-1:
+//       nbw/2            w-pairs    (t, h, 2wp) + (t, h, 2wp+1);
+//       if nbw is odd    the block  (t, h, nbw-1) alone.
+__host__ __device__ inline int groups_per_head_of(int nbt, int nbh, int nbw) {
+  return (nbt / 2) * nbh * nbw +
+         (nbt % 2) * ((nbh / 2) * nbw + (nbh % 2) * (nbw / 2 + nbw % 2));
+}
+
+// Leader block and partner (or -1) of work item gl of a head (order above).
 __host__ __device__ inline void group_blocks(const Geo& g, int gl, int* lead, int* partner) {
-  int i, c, n;
-  if (g.pair_axis == 0) {
-    const int plane = g.nbh * g.nbw, tg = gl / plane;
-    i = gl + tg * plane; c = 2 * tg; n = g.nbt;
-  } else if (g.pair_axis == 1) {
-    const int hh = (g.nbh + 1) / 2, wb = gl % g.nbw, hg = (gl / g.nbw) % hh, tb = gl / (g.nbw * hh);
-    i = (tb * g.nbh + 2 * hg) * g.nbw + wb; c = 2 * hg; n = g.nbh;
-  } else if (g.pair_axis == 2) {
-    const int wh = (g.nbw + 1) / 2, wg = gl % wh, rest = gl / wh;
-    i = rest * g.nbw + 2 * wg; c = 2 * wg; n = g.nbw;
-  } else {
-    *lead = gl; *partner = -1; return;
+  const int plane = g.nbh * g.nbw;
+  const int n_t = (g.nbt / 2) * plane;
+  if (gl < n_t) {
+    const int tp = gl / plane;
+    *lead = gl + tp * plane;          // (2tp) * plane + (gl % plane)
+    *partner = *lead + plane;
+    return;
   }
-  *lead = i;
-  *partner = (c + 1 < n) ? i + g.pair_stride : -1;
+  gl -= n_t;
+  int base = (g.nbt - 1) * plane;     // the last t-plane (nbt odd)
+  const int n_h = (g.nbh / 2) * g.nbw;
+  if (gl < n_h) {
+    const int hp = gl / g.nbw, wb = gl % g.nbw;
+    *lead = base + 2 * hp * g.nbw + wb;
+    *partner = *lead + g.nbw;
+    return;
+  }
+  gl -= n_h;
+  base += (g.nbh - 1) * g.nbw;        // its last h-row (nbh odd)
+  if (gl < g.nbw / 2) {
+    *lead = base + 2 * gl;
+    *partner = *lead + 1;
+    return;
+  }
+  *lead = base + g.nbw - 1;           // nbw odd: the last block alone
+  *partner = -1;
 }
 
 // Route workspace layout (byte offsets, all 256-aligned).

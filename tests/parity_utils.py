@@ -126,29 +126,36 @@ def compare_outputs(o_gpu: np.ndarray, o_ref: np.ndarray, geo, rows, H: int, dty
 
 
 def pair_groups(geo, heads: int):
-    """Work items of the bf16 attention kernel: query blocks paired with their
-    neighbour along t (else h, else w); a block with an even coordinate on that
-    axis leads, its successor (if any) is the partner.  Items are listed head
-    by head, leaders in ascending block order.  Returns [(row_a, row_b or -1)]."""
+    """Work items of the bf16 attention kernel, head by head: t-neighbour pairs
+    (even t leads) over the first 2*(nbt//2) planes; if nbt is odd, the last
+    plane's h-neighbour pairs (even h leads); if nbh is odd too, that plane's
+    last row's w-neighbour pairs (even w leads); if nbw is odd as well, the
+    last block alone.  Returns [(row_a, row_b or -1)]."""
     nbt, nbh, nbw = geo.nblk
-    if nbt >= 2:
-        axis, stride, n = 0, nbh * nbw, nbt
-    elif nbh >= 2:
-        axis, stride, n = 1, nbw, nbh
-    elif nbw >= 2:
-        axis, stride, n = 2, 1, nbw
-    else:
-        axis = None
+
+    def blk(t, h, w):
+        return (t * nbh + h) * nbw + w
+
+    per_head = []
+    for tp in range(nbt // 2):
+        for h in range(nbh):
+            for w in range(nbw):
+                per_head.append((blk(2 * tp, h, w), blk(2 * tp + 1, h, w)))
+    if nbt % 2:
+        t = nbt - 1
+        for hp in range(nbh // 2):
+            for w in range(nbw):
+                per_head.append((blk(t, 2 * hp, w), blk(t, 2 * hp + 1, w)))
+        if nbh % 2:
+            h = nbh - 1
+            for wp in range(nbw // 2):
+                per_head.append((blk(t, h, 2 * wp), blk(t, h, 2 * wp + 1)))
+            if nbw % 2:
+                per_head.append((blk(t, h, nbw - 1), -1))
     out = []
     for bh in range(heads):
-        for i in range(geo.nb):
-            if axis is None:
-                out.append((bh * geo.nb + i, -1))
-                continue
-            coord = (i // (nbh * nbw), (i // nbw) % nbh, i % nbw)[axis]
-            if coord % 2 == 0:
-                partner = bh * geo.nb + i + stride if coord + 1 < n else -1
-                out.append((bh * geo.nb + i, partner))
+        for a, b in per_head:
+            out.append((bh * geo.nb + a, bh * geo.nb + b if b >= 0 else -1))
     return out
 
 

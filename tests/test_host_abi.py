@@ -257,3 +257,26 @@ def test_default_sched(cfg, want):
     plan = A.plan_init(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.block, wl.dtype)
     assert A.default_sched(plan) == want
     assert _lib().abs_attend_default_sched(ctypes.byref(plan), None) == A.EINVAL
+
+
+@pytest.mark.parametrize("grid,block", [((21, 30, 52), (2, 8, 8)), ((5, 12, 20), (2, 8, 8)),
+                                        ((2, 8, 40), (2, 8, 8)), ((9, 10, 11), (4, 4, 4)),
+                                        ((3, 13, 21), (1, 8, 16)), ((2, 8, 8), (2, 8, 8))])
+def test_work_items_cover_every_block_once(grid, block):
+    # the test-side mirror of the work-item rule: every query block in exactly
+    # one item, partners are neighbours along one axis, and the library plans
+    # the same number of items
+    from parity_utils import pair_groups
+    geo = O.geometry(grid, block)
+    items = pair_groups(geo, 1)
+    seen = [r for pair in items for r in pair if r >= 0]
+    assert sorted(seen) == list(range(geo.nb))
+    nbt, nbh, nbw = geo.nblk
+    for a, b in items:
+        if b < 0:
+            continue
+        ca = (a // (nbh * nbw), (a // nbw) % nbh, a % nbw)
+        cb = (b // (nbh * nbw), (b // nbw) % nbh, b % nbw)
+        d = [y - x for x, y in zip(ca, cb)]
+        assert sorted(d) == [0, 0, 1] and ca[d.index(1)] % 2 == 0
+    assert sum(1 for _, b in items if b < 0) <= 1
