@@ -508,14 +508,15 @@ __global__ void reset_counter_kernel(int* counter) {
 
 // ---------------------------------------------------------------------------
 // bf16 block-sparse attention.  A workgroup handles one work item: a pair of
-// neighbouring query blocks of one head (or a single block), 4 waves per
+// neighbouring query blocks of one head (or a single block, see
+// group_blocks), 4 waves per
 // query block (BT = 128), wave w owning one 32-query subtile of block w/NW1
 // (subtile w%NW1, rotated by two in the second block).  The workgroup walks
 // the union of the two ascending kept-block lists
 // (precomputed per item by tile_list_kernel and read two entries ahead);
 // each K/V tile is copied into LDS once and serves both blocks that keep it
 // (neighbouring blocks keep nearly the same key blocks: at 480p a copy serves
-// 1.7 blocks on average).  Per kept key block j, for the waves whose block keeps j, in chunks
+// 1.85 blocks on average).  Per kept key block j, for the waves whose block keeps j, in chunks
 // of 64 keys:
 //   S^T (keys x queries) = K_j Q^T with v_mfma_f32_32x32x16_bf16 (Q^T held in
 //     registers as the B operand, K_j read from LDS as the A operand);

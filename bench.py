@@ -46,16 +46,24 @@ def imbalance(tel: np.ndarray):
                 busy_max_over_mean=float(b.max() / b.mean()))
 
 
-def code_digest(path: str) -> str:
-    """sha256 of a C++/HIP source with its comments and blank space removed:
+def code_digest(*paths: str) -> str:
+    """sha256 of C++/HIP sources with their comments and blank space removed:
     it changes when the code changes, not when only a comment does."""
     import hashlib
     import re
-    text = open(path).read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", "", text)
-    text = "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
-    return hashlib.sha256(text.encode()).hexdigest()
+    parts = []
+    for path in paths:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        parts.append("\n".join(" ".join(line.split()) for line in text.splitlines()
+                               if line.strip()))
+    return hashlib.sha256("\n\f\n".join(parts).encode()).hexdigest()
+
+
+# the sources compiled into the attention kernel
+ATTEND_SOURCES = [os.path.join(ROOT, "adaptive_block_sparse_amd", "csrc", f)
+                  for f in ("attend.hip", "internal.h", "device_common.h")]
 
 
 def measured_traffic(workload_cfg: int, sched: str):
@@ -63,7 +71,6 @@ def measured_traffic(workload_cfg: int, sched: str):
     FETCH_SIZE/WRITE_SIZE summary, if it was taken on this workload and launch
     and the kernel code has not changed since (else None)."""
     path = os.path.join(ROOT, "profiles", "attn_bf16_wan22_480p_hbm_traffic.md")
-    src = os.path.join(ROOT, "adaptive_block_sparse_amd", "csrc", "attend.hip")
     if workload_cfg != 1 or not os.path.exists(path):
         return None
     fields = {}
@@ -71,7 +78,8 @@ def measured_traffic(workload_cfg: int, sched: str):
         if ":" in line and not line.startswith((" ", "|", "#")):
             key, _, val = line.partition(":")
             fields[key.strip()] = val.strip()
-    if (fields.get("attend_hip_code_sha256") != code_digest(src) or fields.get("sched") != sched
+    if (fields.get("attend_code_sha256") != code_digest(*ATTEND_SOURCES)
+            or fields.get("sched") != sched
             or "traffic_bytes_per_launch" not in fields):
         return None
     return int(fields["traffic_bytes_per_launch"])
