@@ -797,6 +797,12 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
           // and PV products run (else its scores are the padding bias alone and
           // its probabilities zero)
           const bool two = C::CHS == 1 || (hc * C::CHS + 1) * 32 < nreal;
+          // Waves w and w + NW1 share a SIMD and would otherwise run the same
+          // phases in step.  Their priorities alternate: chunk by chunk, one
+          // half leads the score products and the other the softmax and PV
+          // products, so that neither trails the other into the tile barrier.
+          const bool lead_qk = ((hc + half) & 1) != 0;
+          if (lead_qk) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
           // ---- S^T = K Q^T for the CHS key subtiles of this chunk
           f32x16_t s[C::CHS];
           // K operands read from LDS 4 products ahead of use (the order of the
@@ -843,6 +849,7 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
             }
           }
 
+          if (lead_qk) __builtin_amdgcn_s_setprio(0); else __builtin_amdgcn_s_setprio(1);
           // ---- online softmax over the chunk's keys, per query column
           // four independent partial maxima (short dependency chains)
           float mq[4];
