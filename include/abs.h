@@ -185,11 +185,14 @@ abs_status abs_slack_budget(const abs_plan* plan, int32_t sched, const int64_t* 
 /* Attention prologue: re-lays k and v block-major for the attention kernel
  * (bf16) and builds the order of `sched` over the attention work items from
  * the mask's row lengths (explainer "Core method" part 2: profile the mask
- * size per head, heaviest first).  A bf16 work item is a pair of query blocks
- * of one head that are neighbours along t (else h, else w): the block with an
- * even coordinate on that axis and its successor, or that block alone at the
- * end of an odd axis; items are numbered head by head, leaders in ascending
- * block order, and an item's cost is the kept-block count of its rows.  On
+ * size per head, heaviest first).  A bf16 work item is a pair of
+ * neighbouring query blocks of one head.  Items are numbered head by head:
+ * first the t-pairs (the block with an even t coordinate and its successor;
+ * plane pair by plane pair, blocks in row-major (h, w) order); if nbt is odd,
+ * the last t-plane's h-pairs (even h and its successor; row pair by row pair,
+ * w ascending); if nbh is odd too, that plane's last row's w-pairs (even w and
+ * its successor); if nbw is odd as well, its last block alone.  An item's cost
+ * is the kept-block count of its rows.  On
  * return (stream order) the workspace starts with the item order, int32
  * [items].  Float32 plans process rows in natural order.
  *   k, v : device [B, N, H, d] of the plan's dtype
