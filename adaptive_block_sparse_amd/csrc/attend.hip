@@ -722,9 +722,10 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
       }
 #pragma unroll
       for (int rr = 0; rr < C::ROUNDS; ++rr) {
-        if (rr >= V2 && short_blk) break;
-        const int off = (rr * C::NW + w) * 1024;
-        dma16(vs + off + lane * 16, sV_base + buf * C::TILE + off);
+        if (rr < V2 || !short_blk) {
+          const int off = (rr * C::NW + w) * 1024;
+          dma16(vs + off + lane * 16, sV_base + buf * C::TILE + off);
+        }
       }
     };
 
