@@ -51,6 +51,9 @@ SMALL = {
     # several extents all occur
     "bf16-block-4x4x8": _wl(114, (7, 10, 13), (4, 4, 8), 3, 128, "bf16"),
     "bf16-block-1x8x16": _wl(115, (3, 13, 21), (1, 8, 16), 2, 128, "bf16"),
+    # 3 x 3 x 5 blocks: t-pairs, then h-pairs in the last plane, w-pairs in its
+    # last row and one block alone, so every tier of the work-item rule runs
+    "bf16-pair-tiers": _wl(116, (5, 20, 40), (2, 8, 8), 2, 128, "bf16"),
     "f32-d64-bt128": _wl(112, (3, 9, 10), (2, 8, 8), 2, 64, "f32"),
 }
 

@@ -42,6 +42,7 @@ SMALL = {
     "pair-w-odd": _wl(109, (2, 8, 40), (2, 8, 8), 2, 128),
     "block-4x4x4": _wl(111, (9, 10, 11), (4, 4, 4), 2, 128),
     "block-4x4x8": _wl(114, (7, 10, 13), (4, 4, 8), 3, 128),
+    "pair-tiers": _wl(116, (5, 20, 40), (2, 8, 8), 2, 128),
 }
 
 
