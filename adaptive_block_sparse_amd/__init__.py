@@ -22,7 +22,7 @@ from typing import Optional, Sequence
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("ABS_LIBRARY") or os.path.join(HERE, "libabs.so")
 
-OK, EINVAL, ENOTSUP, ENOSPACE, EHIP = 0, 1, 2, 3, 4
+OK, EINVAL, ENOTSUP, ENOSPACE, EHIP, ETOOBIG = 0, 1, 2, 3, 4, 5
 F32, BF16 = 0, 1
 SCHED_NNZ_SORTED, SCHED_HEAD_MAJOR, SCHED_HEAD_PHASED, SCHED_XCD_LOCAL = 0, 1, 2, 3
 SCHEDULES = {"nnz_sorted": SCHED_NNZ_SORTED, "head_major": SCHED_HEAD_MAJOR,
@@ -31,7 +31,9 @@ EXPORTS = ("abs_plan_init", "abs_route", "abs_attend_prepare", "abs_attend_run",
            "abs_attend", "abs_attend_grid", "abs_status_string", "abs_attend_split_ws_bytes",
            "abs_attend_prepare_split", "abs_attend_run_split", "abs_route_dynamic",
            "abs_slack_budget", "abs_attend_relayout", "abs_attend_schedule",
-           "abs_attend_default_sched")
+           "abs_attend_default_sched", "abs_route_noalloc")
+# bytes of the static device scratch abs_route_noalloc works in (include/abs.h)
+ROUTE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class Shape(ctypes.Structure):
@@ -89,6 +91,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "abs_attend_relayout": [P, V, V, V, SZ, V],
         "abs_attend_schedule": [P, M, I32, V, SZ, V],
         "abs_slack_budget": [P, I32, V, F, ctypes.c_int64, V, V],
+        "abs_route_noalloc": [P, V, V, F, I32, F, M, V],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -188,6 +191,22 @@ def route(plan: Plan, q, k, p: float, k_floor: int, slack: float = 0.0,
                                   float(slack), ctypes.byref(cm), _ptr(ws), ws.numel(),
                                   _stream(stream))
     _check("abs_route", st)
+    return mask
+
+
+def route_noalloc(plan: Plan, q, k, p: float, k_floor: int, slack: float = 0.0,
+                  mask: Optional[Mask] = None, stream=None) -> Mask:
+    """route() without a workspace argument: the library works in its static
+    per-GPU device scratch and allocates nothing (the mask buffers are the
+    caller's; pass `mask` to allocate nothing here either).  Calls that overlap
+    on one GPU race."""
+    _check_qkv(plan, q, k)
+    mask = Mask(plan, q.device) if mask is None else mask
+    cm = mask.c()
+    st = load_library().abs_route_noalloc(ctypes.byref(plan), _ptr(q), _ptr(k), float(p),
+                                          int(k_floor), float(slack), ctypes.byref(cm),
+                                          _stream(stream))
+    _check("abs_route_noalloc", st)
     return mask
 
 

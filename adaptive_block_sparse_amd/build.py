@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libabs.so")
-SOURCES = ["api.hip", "route.hip", "attend.hip"]
+SOURCES = ["api.hip", "route.hip", "attend.hip", "noalloc.hip"]
 # measurement aid (sustained MFMA rate and clock), a library of its own
 PROBE_LIB = os.path.join(HERE, "libabs_probe.so")
 PROBE_SOURCES = ["probe.hip"]

@@ -109,6 +109,7 @@ const char* abs_status_string(abs_status st) {
     case ABS_ENOTSUP: return "unsupported shape or dtype";
     case ABS_ENOSPACE: return "workspace too small";
     case ABS_EHIP: return "HIP launch error";
+    case ABS_ETOOBIG: return "plan too large for the static no-allocation scratch";
   }
   return "unknown status";
 }

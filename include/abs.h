@@ -56,7 +56,8 @@ typedef enum {
   ABS_EINVAL = 1,   /* null pointer, non-positive size, p outside (0,1], ... */
   ABS_ENOTSUP = 2,  /* head_dim, block size, dtype or size outside the built kernels */
   ABS_ENOSPACE = 3, /* workspace smaller than the plan requires */
-  ABS_EHIP = 4      /* HIP launch error */
+  ABS_EHIP = 4,     /* HIP launch error */
+  ABS_ETOOBIG = 5   /* the plan needs more than the static scratch of abs_route_noalloc */
 } abs_status;
 
 typedef enum { ABS_F32 = 0, ABS_BF16 = 1 } abs_dtype;
@@ -291,6 +292,31 @@ abs_status abs_attend_prepare_split(const abs_plan* plan, const void* k, const v
 abs_status abs_attend_run_split(const abs_plan* plan, const void* q, const abs_mask* mask,
                                 void* o, int32_t sched, int32_t max_parts, void* ws,
                                 size_t ws_bytes, int64_t* telemetry, void* stream);
+
+/* Bytes of the static device scratch that abs_route_noalloc works in. */
+#define ABS_ROUTE_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/* abs_route for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, computation and result as abs_route, but no workspace argument:
+ * the route workspace is a static device array of
+ * ABS_ROUTE_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on every GPU
+ * it runs on until the process ends.  The call allocates and frees nothing
+ * (no hipMalloc, hipFree or allocating library routine).
+ *   Size limit: the workspace abs_route needs for this plan and slack must fit
+ *   the scratch; plan->route_ws_bytes (the need with the fill) bounds it.
+ *   A larger plan returns ABS_ETOOBIG before any device call.
+ *   Sharing: every call on one GPU works in that GPU's one array, which keeps
+ *   the last call's contents (nothing in it has to start at zero: each call
+ *   writes what it reads).  Calls that overlap in time on one GPU (several
+ *   streams or host threads) race and give undefined masks; order them on one
+ *   stream or with events.
+ *   stream : hipStream_t of the current device (NULL = its default stream);
+ *            a stream of another device returns ABS_EINVAL.
+ * Errors as abs_route (ABS_ENOSPACE cannot occur), plus ABS_ETOOBIG, and
+ * ABS_EHIP if the scratch address cannot be obtained. */
+abs_status abs_route_noalloc(const abs_plan* plan, const void* q, const void* k, float p,
+                             int32_t k_floor, float slack, const abs_mask* mask, void* stream);
 
 /* Static description of a status code. */
 const char* abs_status_string(abs_status status);

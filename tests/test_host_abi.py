@@ -280,3 +280,31 @@ def test_work_items_cover_every_block_once(grid, block):
         d = [y - x for x, y in zip(ca, cb)]
         assert sorted(d) == [0, 0, 1] and ca[d.index(1)] % 2 == 0
     assert sum(1 for _, b in items if b < 0) <= 1
+
+
+def _route_noalloc(plan, q=FAKE, k=FAKE, p=0.9, kf=4, slack=0.0, mask=True):
+    lib = _lib()
+    cm = A.CMask(0x100000, 0x200000, 0x300000)
+    return lib.abs_route_noalloc(ctypes.byref(plan), q, k, p, kf, slack,
+                                 ctypes.byref(cm) if mask else None, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(p=0.0), A.EINVAL), (dict(p=math.nan), A.EINVAL), (dict(kf=0), A.EINVAL),
+    (dict(slack=1.0), A.EINVAL), (dict(q=None), A.EINVAL), (dict(mask=False), A.EINVAL),
+])
+def test_route_noalloc_validation(kw, want):
+    assert _route_noalloc(_plan(), **kw) == want
+
+
+def test_route_noalloc_rejects_plans_beyond_its_scratch():
+    # 720p with 40 heads: the route workspace exceeds the 64 MiB static scratch;
+    # the call must say so before touching a device
+    _lib()
+    wl = si.WORKLOADS[2]
+    plan = A.plan_init(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.block, wl.dtype)
+    assert plan.route_ws_bytes > A.ROUTE_NOALLOC_SCRATCH_BYTES
+    assert _route_noalloc(plan, slack=0.15) == A.ETOOBIG
+    assert A.status_string(A.ETOOBIG) == "plan too large for the static no-allocation scratch"
+    header = open(os.path.join(ROOT, "include", "abs.h")).read()
+    assert re.search(r"#define ABS_ROUTE_NOALLOC_SCRATCH_BYTES \(64ull << 20\)", header)
