@@ -43,10 +43,11 @@ RouteWs route_ws_layout(const Geo& g, bool slack) {
   const size_t pooled = (size_t)g.B * g.H * g.nb * g.d * sizeof(float);
   L.qp = take(pooled);
   L.kp = take(pooled);
-  L.score = take((size_t)g.rows * g.nb * sizeof(float));
+  L.prob = take(slack ? (size_t)g.rows * g.nb * sizeof(float) : 0);
   L.bitmap = take((size_t)g.rows * g.words * sizeof(uint32_t));
   L.count = take((size_t)g.rows * sizeof(int));
   const size_t heads = (size_t)g.B * g.H;
+  L.gsum = take(heads * route_groups_per_head(g.nb) * sizeof(int));
   L.hist = take(slack ? heads * 2048 * sizeof(uint32_t) : 0);
   L.sel = take(slack ? heads * 4 * sizeof(int) : 0);
   L.eqcnt = take(slack ? (size_t)g.rows * sizeof(int) : 0);

@@ -1,8 +1,9 @@
-// Routing kernels: 3D-block mean pooling, pooled block scores, per-row Top-p
-// selection with a Top-k floor and own-block repair, per-head slack fill, and
-// CSR compaction.  Source: FVAttn explainer ("FVAttn: adaptive sparse
-// attention with runtime load balancing, for video generation"), "Core method"
-// part 1 (sparse-routing frontend) and part 3 (slack-aware augmentation).
+// Routing kernels: 3D-block mean pooling, pooled block scores with a row
+// softmax and the per-row Top-p selection (Top-k floor, own-block repair) in
+// one pass, per-head slack fill, and CSR compaction.  Source: FVAttn explainer
+// ("FVAttn: adaptive sparse attention with runtime load balancing, for video
+// generation"), "Core method" part 1 (sparse-routing frontend) and part 3
+// (slack-aware augmentation).
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -15,353 +16,592 @@ namespace abs_impl {
 // ---------------------------------------------------------------------------
 // Pooling: mean of Q and K over the real tokens of each 3D block (the cheap
 // approximate similarity the routing runs on, explainer "Highlights and
-// limitations").  One workgroup per (block, batch*head); 16-byte coalesced
-// loads of each token's d-vector; float32 sums in a fixed order.
+// limitations").  One workgroup per (3D block, group of hg heads of one batch
+// entry).  In the [B, N, H, d] layout a token's heads sit side by side, so for
+// every real token of the block the workgroup reads one contiguous run of
+// hg*d elements, and the workgroups of the other head groups of the same block
+// (launched next to it) read the rest of those tokens' rows.  Each thread owns
+// one 16-byte chunk of the run and a residue class of the block's slots; it
+// keeps 16 loads in flight and sums in slot order, then the classes are summed
+// in a fixed order through LDS.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_kernel(Geo g, const T* __restrict__ q,
                                                    const T* __restrict__ k,
                                                    float* __restrict__ qp,
-                                                   float* __restrict__ kp) {
+                                                   float* __restrict__ kp, int hg) {
   constexpr int E = Chunk<T>::E;   // elements per 16-byte chunk
-  constexpr int C = D / E;         // chunks per token row
-  constexpr int G = 256 / C;       // token groups
-  __shared__ float red[G][D];
-  const int blk = blockIdx.x, bh = blockIdx.y;
-  const int b = bh / g.H, h = bh % g.H;
+  constexpr int C = D / E;         // chunks per head
+  constexpr int BATCH = 8;         // slots per batch of loads (per tensor)
+  __shared__ float red[2][256 * E];
+  const int run = hg * C;          // chunks per token run; divides 256
+  const int tpp = 256 / run;       // slots per pass
+  const int ngrp = g.H / hg;
+  const int b = blockIdx.x / ngrp, h0 = (blockIdx.x % ngrp) * hg;
+  const int blk = blockIdx.y;
   const int tb = blk / (g.nbh * g.nbw), hb = (blk / g.nbw) % g.nbh, wb = blk % g.nbw;
   const int Tl = min(g.bt, g.T - tb * g.bt), Hl = min(g.bh, g.Hg - hb * g.bh),
             Wl = min(g.bw, g.W - wb * g.bw);
   const float inv = 1.0f / (float)(Tl * Hl * Wl);
-  const int c = threadIdx.x % C, grp = threadIdx.x / C;
+  const int c = threadIdx.x % run, sub = threadIdx.x / run;
   const int plane = g.bh * g.bw;
-#pragma unroll 1
-  for (int which = 0; which < 2; ++which) {
-    const T* src = which == 0 ? q : k;
-    float* dst = which == 0 ? qp : kp;
-    float acc[E];
+  const long tok = (long)g.H * D;                  // elements per token row
+  const long base = (long)b * g.N * tok + (long)h0 * D + c * E;
+  float aq[E], ak[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    // every load of this thread is issued before the first sum (the slots a
-    // thread visits are at most 128 / G); padding slots contribute zeros, and
-    // the sums run in slot order
-    constexpr int MAXIT = 128 / G;
-    uint4 raw[MAXIT];
+  for (int e = 0; e < E; ++e) aq[e] = ak[e] = 0.f;
+  for (int s0 = sub; s0 < g.Bt; s0 += BATCH * tpp) {
+    uint4 rq[BATCH], rk[BATCH];
 #pragma unroll
-    for (int it = 0; it < MAXIT; ++it) {
-      const int s = grp + it * G;
-      raw[it] = make_uint4(0u, 0u, 0u, 0u);
+    for (int u = 0; u < BATCH; ++u) {
+      const int s = s0 + u * tpp;
+      rq[u] = rk[u] = make_uint4(0u, 0u, 0u, 0u);
       const int st = s / plane, sh = (s / g.bw) % g.bh, sw = s % g.bw;
       if (s < g.Bt && st < Tl && sh < Hl && sw < Wl) {
         const long n = ((long)(tb * g.bt + st) * g.Hg + hb * g.bh + sh) * g.W + wb * g.bw + sw;
-        raw[it] = *reinterpret_cast<const uint4*>(src + (((long)b * g.N + n) * g.H + h) * D + c * E);
+        rq[u] = *reinterpret_cast<const uint4*>(q + base + n * tok);
+        rk[u] = *reinterpret_cast<const uint4*>(k + base + n * tok);
       }
     }
 #pragma unroll
-    for (int it = 0; it < MAXIT; ++it) {
-      float v[E];
-      Chunk<T>::unpack(raw[it], v);
+    for (int u = 0; u < BATCH; ++u) {
+      float vq[E], vk[E];
+      Chunk<T>::unpack(rq[u], vq);
+      Chunk<T>::unpack(rk[u], vk);
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += v[e];
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) red[grp][c * E + e] = acc[e];
-    __syncthreads();
-    for (int dd = threadIdx.x; dd < D; dd += 256) {
-      float s = 0.f;
-      for (int gg = 0; gg < G; ++gg) s += red[gg][dd];
-      dst[((long)bh * g.nb + blk) * D + dd] = s * inv;
-    }
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Pooled block scores S[b,h,i,j] = Qp_i . Kp_j / sqrt(d), float32.  64x64
-// output tile per workgroup, 4x4 per thread, d consumed in slices of 32.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void scores_kernel(Geo g, const float* __restrict__ qp,
-                                                     const float* __restrict__ kp,
-                                                     float* __restrict__ score, float scale) {
-  __shared__ float As[32][64 + 4];
-  __shared__ float Bs[32][64 + 4];
-  const int bh = blockIdx.z;
-  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
-  const float* Q = qp + (long)bh * g.nb * D;
-  const float* K = kp + (long)bh * g.nb * D;
-  float acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[a][c] = 0.f;
-  for (int d0 = 0; d0 < D; d0 += 32) {
-    // 64 rows x 32 columns of each operand, stored transposed (d-major)
-    for (int e = threadIdx.x; e < 64 * 32; e += 256) {
-      const int r = e / 32, dd = e % 32;
-      As[dd][r] = (i0 + r < g.nb) ? Q[(long)(i0 + r) * D + d0 + dd] : 0.f;
-      Bs[dd][r] = (j0 + r < g.nb) ? K[(long)(j0 + r) * D + d0 + dd] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int dd = 0; dd < 32; ++dd) {
-      float a[4], bb[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) { a[x] = As[dd][ty * 4 + x]; bb[x] = Bs[dd][tx * 4 + x]; }
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(a[x], bb[y], acc[x][y]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int i = i0 + ty * 4 + x;
-    if (i >= g.nb) continue;
-#pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int j = j0 + tx * 4 + y;
-      if (j < g.nb) score[((long)bh * g.nb + i) * g.nb + j] = acc[x][y] * scale;
+      for (int e = 0; e < E; ++e) {
+        aq[e] += vq[e];
+        ak[e] += vk[e];
+      }
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// Per-row selection.  P = softmax of the score row; blocks sorted by
-// (P descending, index ascending) with a bitonic sort of 64-bit keys in LDS;
-// an inclusive scan of the sorted masses finds m, the smallest count reaching
-// p; keep the first min(nb, max(m, k_floor)) blocks plus the own block.
-// Output: the row's kept-block bitmap and count (and P, for the slack fill).
-// ---------------------------------------------------------------------------
-template <int NBP>
-__global__ __launch_bounds__(256) void select_kernel(Geo g, float* __restrict__ score,
-                                                     uint32_t* __restrict__ bitmap,
-                                                     int* __restrict__ count, float p,
-                                                     int k_floor, int write_prob) {
-  constexpr int NT = 256;
-  __shared__ unsigned long long keys[NBP];
-  __shared__ float ev[NBP];
-  __shared__ uint32_t bits[NBP / 32];
-  __shared__ float ftmp[NT / 64 + 1];
-  __shared__ int itmp[NT / 64 + 1];
-  const int row = blockIdx.x;
-  const int nb = g.nb;
-  const int i = row % nb;
-  float* srow = score + (long)row * nb;
-
-  float mx = -INFINITY;
-  for (int j = threadIdx.x; j < nb; j += NT) mx = fmaxf(mx, srow[j]);
-  mx = block_max<NT>(mx, ftmp);
-  float part = 0.f;
-  for (int j = threadIdx.x; j < nb; j += NT) {
-    const float e = expf(srow[j] - mx);
-    ev[j] = e;
-    part += e;
+  // thread (sub, c) holds outputs o = c*E + e of the run: head h0 + o / D, dim o % D
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    red[0][threadIdx.x * E + e] = aq[e];
+    red[1][threadIdx.x * E + e] = ak[e];
   }
-  const float z = block_sum<NT>(part, ftmp);
-  for (int j = threadIdx.x; j < NBP; j += NT) {
-    unsigned long long key = ~0ull;
-    if (j < nb) {
-      const float pj = ev[j] / z;
-      if (write_prob) srow[j] = pj;
-      key = ((unsigned long long)(~__float_as_uint(pj)) << 32) | (unsigned)j;
-    }
-    keys[j] = key;
-  }
-  for (int w = threadIdx.x; w < NBP / 32; w += NT) bits[w] = 0u;
   __syncthreads();
+  const int outs = run * E;
+  for (int o = threadIdx.x; o < 2 * outs; o += 256) {
+    const int which = o / outs, oo = o % outs;
+    float sum = 0.f;
+    for (int s = 0; s < tpp; ++s) sum += red[which][s * outs + oo];
+    float* dst = which == 0 ? qp : kp;
+    dst[(((long)b * g.H + h0 + oo / D) * g.nb + blk) * D + oo % D] = sum * inv;
+  }
+}
 
-  // bitonic sort, ascending keys = P descending then index ascending
-  for (int size = 2; size <= NBP; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = threadIdx.x; t < NBP / 2; t += NT) {
-        const int lo = 2 * t - (t & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const unsigned long long a = keys[lo], c = keys[hi];
-        if ((a > c) == up) { keys[lo] = c; keys[hi] = a; }
+// ---------------------------------------------------------------------------
+// Wave-wide sum and maximum through DPP row operations (quad swaps, half-row
+// and row mirrors) and the four row results read out in a fixed order, so
+// every lane receives the same value.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_lanes(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x += dpp_f<0xb1>(x);    // quad_perm [1,0,3,2]
+  x += dpp_f<0x4e>(x);    // quad_perm [2,3,0,1]
+  x += dpp_f<0x141>(x);   // row_half_mirror
+  x += dpp_f<0x140>(x);   // row_mirror: every lane of a row of 16 holds the row sum
+  return (row_lanes(x, 0) + row_lanes(x, 16)) + (row_lanes(x, 32) + row_lanes(x, 48));
+}
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = fmaxf(x, dpp_f<0xb1>(x));
+  x = fmaxf(x, dpp_f<0x4e>(x));
+  x = fmaxf(x, dpp_f<0x141>(x));
+  x = fmaxf(x, dpp_f<0x140>(x));
+  return fmaxf(fmaxf(row_lanes(x, 0), row_lanes(x, 16)),
+               fmaxf(row_lanes(x, 32), row_lanes(x, 48)));
+}
+__device__ __forceinline__ int popc_ballot(bool b) { return __popcll(__ballot(b)); }
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Sum and maximum over each row of 16 lanes (DPP quad swaps, half-row and row
+// mirrors): every lane of a row receives its row's result.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0xb1>(x);
+  x += dpp_f<0x4e>(x);
+  x += dpp_f<0x141>(x);
+  x += dpp_f<0x140>(x);
+  return x;
+}
+__device__ __forceinline__ int row16_sum_int(int x) {
+  x += dpp_i<0xb1>(x);
+  x += dpp_i<0x4e>(x);
+  x += dpp_i<0x141>(x);
+  x += dpp_i<0x140>(x);
+  return x;
+}
+__device__ __forceinline__ int row16_max_int(int x) {
+  x = max(x, dpp_i<0xb1>(x));
+  x = max(x, dpp_i<0x4e>(x));
+  x = max(x, dpp_i<0x141>(x));
+  x = max(x, dpp_i<0x140>(x));
+  return x;
+}
+__device__ __forceinline__ int row16_min_int(int x) {
+  x = min(x, dpp_i<0xb1>(x));
+  x = min(x, dpp_i<0x4e>(x));
+  x = min(x, dpp_i<0x141>(x));
+  x = min(x, dpp_i<0x140>(x));
+  return x;
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<0xb1>(x));
+  x = fmaxf(x, dpp_f<0x4e>(x));
+  x = fmaxf(x, dpp_f<0x141>(x));
+  x = fmaxf(x, dpp_f<0x140>(x));
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// Scores, softmax and Top-p selection of 16 rows (query blocks) of one head,
+// nb <= 64*NC <= 1024 (one workgroup; wave w owns rows 4w..4w+3 of the group).
+//
+// Scores: Kp of the head streams through LDS in chunks of 64 key blocks, and
+// each wave multiplies the group's 16 Qp rows by 16 of a chunk's keys on the
+// fp32 matrix cores.  The scores then pass through LDS so that row r of wave w
+// (group row 4w + r) lives in lanes 16r..16r+15 (one DPP row), element
+// j = 16e + (lane & 15) in register e.  Every step below works on the wave's
+// four rows at once and reduces within DPP rows.
+//
+// Selection.  The probabilities are never sorted.  The order (P descending,
+// then j ascending) is only needed through two of its consequences, both found
+// by bisection over the float32 bit pattern of P (non-negative floats order
+// like their bits; 30 halvings of [0, bits(1.0) + 1]):
+//   mass:  the largest t with S(t) = sum of P_j over bits(P_j) >= t at least
+//          p is the bit pattern of the m-th largest P, where m is the size of
+//          the smallest prefix of the order reaching p; the blocks above it are
+//          kept, and of the blocks equal to it the lowest-index ones the prefix
+//          needs;
+//   floor: when m is below k_floor, the largest t with at least k_floor blocks
+//          at or above it, the ties again by lowest index.
+// p = 1, or a total that rounding left below p, keeps every block.  The own
+// block is added last.  Output: the rows' bitmaps and counts, the group's
+// total count (for the CSR offsets) and, for slack fills, P.
+// ---------------------------------------------------------------------------
+template <int D, int NC>
+__global__ __launch_bounds__(256) void route_select_kernel(
+    Geo g, const float* __restrict__ qp, const float* __restrict__ kp,
+    uint32_t* __restrict__ bitmap, int* __restrict__ count, int* __restrict__ gsum,
+    float* __restrict__ prob, float p, int k_floor, float scale) {
+  constexpr int KS = D + 4;          // padded LDS row of one key block's mean
+  constexpr int TS = 64 * NC + 16;   // padded LDS row of one row's scores
+  constexpr int E = 4 * NC;          // elements per lane in the 16-lane layout
+  constexpr int KD = D / 4;          // MFMA k-steps (4 dimensions each)
+  constexpr int LDS_F = 64 * KS > 16 * TS ? 64 * KS : 16 * TS;
+  __shared__ float lds[LDS_F];
+  __shared__ int wsum[4];
+  const int bh = blockIdx.y;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int nb = g.nb;
+  const int nch = (nb + 63) >> 6;    // key chunks present (<= NC)
+  const int ig = blockIdx.x * 16;    // first row of the group
+  const float* K = kp + (long)bh * nb * D;
+  // Scores on the fp32 matrix cores (v_mfma_f32_16x16x4_f32): the group's 16
+  // rows against 16 keys per wave and chunk.  Lane l supplies A[l % 16][l / 16]
+  // and B[l / 16][l % 16] and receives D[4 (l / 16) + r][l % 16] in register r.
+  // k-step s gives slot l / 16 the dimension KD (l / 16) + s, so each lane's A
+  // values (its row's Qp) are KD consecutive floats, loaded once.
+  const int a16 = lane & 15, kq = lane >> 4;
+  float a[KD];
+  {
+    const float4* src = reinterpret_cast<const float4*>(
+        qp + ((long)bh * nb + min(ig + a16, nb - 1)) * D + KD * kq);
+#pragma unroll
+    for (int s = 0; s < KD / 4; ++s) {
+      const float4 v = src[s];
+      a[4 * s] = v.x; a[4 * s + 1] = v.y; a[4 * s + 2] = v.z; a[4 * s + 3] = v.w;
+    }
+  }
+  // chunk c + 1 of Kp is loaded into registers while chunk c is multiplied
+  constexpr int PER = 64 * (D / 4) / 256;   // float4 per thread per chunk
+  float4 nxt[PER];
+  auto load_chunk = [&](int c) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int f = threadIdx.x + 256 * u;
+      const int kb = f / (D / 4), d4 = f % (D / 4);
+      const int j = c * 64 + kb;
+      nxt[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < nb) nxt[u] = *reinterpret_cast<const float4*>(K + (long)j * D + d4 * 4);
+    }
+  };
+  load_chunk(0);
+  v4f acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (c < nch) {
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int f = threadIdx.x + 256 * u;
+        *reinterpret_cast<float4*>(lds + (f / (D / 4)) * KS + (f % (D / 4)) * 4) = nxt[u];
+      }
+      if (c + 1 < nch) load_chunk(c + 1);
+      __syncthreads();
+      const float* brow = lds + (16 * wv + a16) * KS + KD * kq;
+#pragma unroll
+      for (int s = 0; s < KD; s += 4) {
+        const float4 bv = *reinterpret_cast<const float4*>(brow + s);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], bv.x, acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s + 1], bv.y, acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s + 2], bv.z, acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s + 3], bv.w, acc[c], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();   // every wave is done with the staged keys
+  // scores to LDS, row-major over the group's 16 rows
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int j = c * 64 + 16 * wv + a16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      lds[(4 * kq + r) * TS + j] = c < nch && j < nb ? acc[c][r] * scale : -INFINITY;
+  }
+  __syncthreads();
+  const float* T = lds + wv * 4 * TS;
+  const int i0 = ig + 4 * wv;
+  const int rr = lane >> 4, l16 = lane & 15;
+  const int i = i0 + rr;             // this lane's row
+  const bool live = i < nb;
+  const int row = bh * nb + i;
+  float x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = T[rr * TS + 16 * e + l16];
+
+  // softmax over the row's nb blocks; keys = bit patterns of P, -1 past nb
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < E; ++e) mx = fmaxf(mx, x[e]);
+  mx = row16_max(mx);
+  float part = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    x[e] = expf(x[e] - mx);
+    part += x[e];
+  }
+  const float rz = 1.0f / row16_sum(part);
+  int key[E];
+  part = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = 16 * e + l16;
+    const float pj = x[e] * rz;
+    if (prob && live && j < nb) prob[(long)row * nb + j] = pj;
+    key[e] = j < nb ? __float_as_int(pj) : -1;
+    part += j < nb ? pj : 0.f;
+  }
+  const float total = row16_sum(part);
+
+  // mass bisection.  Bracket: S(lo) >= p > S(hi) = shi, clo and chi blocks at
+  // or above lo and hi.  It starts at [bits(min P), bits(max P) + 1) and stops
+  // once one block is left inside it (its P is the cut) or it is one bit wide
+  // (the blocks inside are ties).
+  int kmin = 0x7fffffff, kmax = -1;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    kmin = key[e] >= 0 ? min(kmin, key[e]) : kmin;
+    kmax = max(kmax, key[e]);
+  }
+  int lo = row16_min_int(kmin), hi = row16_max_int(kmax) + 1;
+  int clo = nb, chi = 0;
+  float shi = 0.f;
+  bool active = clo - chi > 1 && hi - lo > 1;
+  for (int step = 0; step < 31; ++step) {
+    if (!__ballot(active)) break;
+    const int mid = lo + ((hi - lo) >> 1);
+    float sp = 0.f;
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool ge = key[e] >= mid;
+      sp += ge ? __int_as_float(key[e]) : 0.f;
+      cnt += ge ? 1 : 0;
+    }
+    const float sm = row16_sum(sp);
+    cnt = row16_sum_int(cnt);
+    const bool up = sm >= p;
+    if (active) {
+      lo = up ? mid : lo;
+      clo = up ? cnt : clo;
+      hi = up ? hi : mid;
+      chi = up ? chi : cnt;
+      shi = up ? shi : sm;
+    }
+    active = clo - chi > 1 && hi - lo > 1;
+  }
+  // the cut: the largest P below hi; the blocks above it, and its ties
+  int kcut = -1;
+#pragma unroll
+  for (int e = 0; e < E; ++e) kcut = key[e] < hi ? max(kcut, key[e]) : kcut;
+  lo = row16_max_int(kcut);
+  const int cg = chi, ct = clo - chi;
+  const float v = __int_as_float(lo);
+  int need = ct;
+  if (v > 0.f) {
+    const float t = ceilf((p - shi) / v);
+    need = t < 1.f ? 1 : (t < (float)ct ? (int)t : ct);
+  }
+  const int m = cg + need;
+  const int m2 = min(nb, max(m, k_floor));
+  const bool all = p >= 1.0f || !(total >= p) || m2 >= nb;
+  const bool floor_row = !all && m2 > m;
+  int thr = all ? -1 : lo;           // keep key > thr, and the first ktie keys == thr
+  int ktie = all ? 0 : need;
+  if (__ballot(floor_row && live)) {
+    // floor: the largest t with at least m2 blocks at or above it
+    int a = 0, b = 0x3f800001;
+    for (int step = 0; step < 30; ++step) {
+      const int mid = a + ((b - a) >> 1);
+      int cnt = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) cnt += key[e] >= mid ? 1 : 0;
+      cnt = row16_sum_int(cnt);
+      const bool up = cnt >= m2;
+      a = up ? mid : a;
+      b = up ? b : mid;
+    }
+    int above = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) above += key[e] > a ? 1 : 0;
+    above = row16_sum_int(above);
+    if (floor_row) {
+      thr = a;
+      ktie = m2 - above;
+    }
+  }
+
+  // kept bits: register e holds keys 16e .. 16e+15 of each row (16 bits of a
+  // 64-bit ballot), so registers 2w and 2w+1 make bitmap word w
+  const uint32_t below = (1u << l16) - 1u;
+  const int sh = 16 * rr;
+  int tie_seen = 0, kept = 0;
+  uint32_t half = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = 16 * e + l16;
+    const bool eq = thr >= 0 && key[e] == thr;
+    const uint32_t eg = (uint32_t)(__ballot(eq) >> sh) & 0xffffu;
+    const int rank = tie_seen + __popc(eg & below);
+    tie_seen += __popc(eg);
+    const bool keep = j < nb && (key[e] > thr || (eq && rank < ktie) || j == i);
+    const uint32_t kg = (uint32_t)(__ballot(keep) >> sh) & 0xffffu;
+    kept += __popc(kg);
+    if (e & 1) {
+      if (live && l16 == 0 && (e >> 1) < g.words) bitmap[(long)row * g.words + (e >> 1)] = half | (kg << 16);
+    } else {
+      half = kg;
+    }
+  }
+  if (live && l16 == 0) count[row] = kept;
+  const int mine = live ? kept : 0;  // the same in all 16 lanes of a row
+  const int wtot = __builtin_amdgcn_readlane(mine, 0) + __builtin_amdgcn_readlane(mine, 16) +
+                   __builtin_amdgcn_readlane(mine, 32) + __builtin_amdgcn_readlane(mine, 48);
+  if (lane == 0) wsum[wv] = wtot;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    gsum[bh * gridDim.x + blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+}
+
+// ---------------------------------------------------------------------------
+// The same scores and selection for nb > 1024 with one wave per row (RPW = 1):
+// element j = 64c + l of the row lives in register c of lane l, and each
+// bisection step reduces across the whole wave.  Same results as above up to
+// the order of float32 sums.
+// ---------------------------------------------------------------------------
+template <int D, int KPL, int RPW>
+__global__ __launch_bounds__(256) void route_select_wide_kernel(
+    Geo g, const float* __restrict__ qp, const float* __restrict__ kp,
+    uint32_t* __restrict__ bitmap, int* __restrict__ count, int* __restrict__ gsum,
+    float* __restrict__ prob, float p, int k_floor, float scale) {
+  constexpr int KS = D + 4;          // padded LDS row of one key block's mean
+  __shared__ float kt[64 * KS];
+  __shared__ int wsum[4];
+  const int bh = blockIdx.y;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int nb = g.nb;
+  const int nch = (nb + 63) >> 6;    // key chunks present (<= KPL)
+  const int i0 = (blockIdx.x * 4 + wv) * RPW;
+  const float* K = kp + (long)bh * nb * D;
+  const float4* Qr[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+    Qr[r] = reinterpret_cast<const float4*>(qp + ((long)bh * nb + min(i0 + r, nb - 1)) * D);
+
+  // scores -> keys: key = bit pattern of P_j, or -1 past nb
+  int key[RPW][KPL];
+#pragma unroll
+  for (int c = 0; c < KPL; ++c) {
+    if (c < nch) {
+      __syncthreads();
+      for (int f = threadIdx.x; f < 64 * (D / 4); f += 256) {
+        const int kb = f / (D / 4), d4 = f % (D / 4);
+        const int j = c * 64 + kb;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j < nb) v = *reinterpret_cast<const float4*>(K + (long)j * D + d4 * 4);
+        *reinterpret_cast<float4*>(kt + kb * KS + d4 * 4) = v;
       }
       __syncthreads();
-    }
-  }
-
-  // inclusive scan of the sorted masses; first position reaching p
-  constexpr int PER = (NBP + NT - 1) / NT;
-  const int r0 = threadIdx.x * PER;
-  float loc[PER];
-  float run = 0.f;
+      float acc[RPW];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int r = r0 + e;
-    const float v = (r < nb) ? __uint_as_float(~(uint32_t)(keys[r] >> 32)) : 0.f;
-    run += v;
-    loc[e] = run;
-  }
-  float tot;
-  const float pre = block_exclusive_scan<NT>(run, ftmp, &tot);
-  int first = nb;  // count m (1-based) of the first prefix reaching p
+      for (int r = 0; r < RPW; ++r) acc[r] = 0.f;
+#pragma unroll 8
+      for (int d4 = 0; d4 < D / 4; ++d4) {
+        const float4 kv = *reinterpret_cast<const float4*>(kt + lane * KS + d4 * 4);
 #pragma unroll
-  for (int e = PER - 1; e >= 0; --e) {
-    const int r = r0 + e;
-    if (r < nb && pre + loc[e] >= p) first = r + 1;
-  }
-  first = -first;
-  {
-    int x = first;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
-    if ((threadIdx.x & 63) == 0) itmp[threadIdx.x >> 6] = x;
-    __syncthreads();
-    int r = itmp[0];
-#pragma unroll
-    for (int w = 1; w < NT / 64; ++w) r = max(r, itmp[w]);
-    first = -r;
-  }
-  const int m = (p >= 1.0f) ? nb : first;
-  const int m2 = min(nb, max(m, k_floor));
-  for (int r = threadIdx.x; r < m2; r += NT) {
-    const int j = (int)(keys[r] & 0xffffffffu);
-    atomicOr(&bits[j >> 5], 1u << (j & 31));
-  }
-  if (threadIdx.x == 0) atomicOr(&bits[i >> 5], 1u << (i & 31));
-  __syncthreads();
-  int pc = 0;
-  for (int w = threadIdx.x; w < g.words; w += NT) {
-    const uint32_t v = bits[w];
-    bitmap[(long)row * g.words + w] = v;
-    pc += __popc(v);
-  }
-  pc = wave_sum_int(pc);
-  if ((threadIdx.x & 63) == 0) itmp[threadIdx.x >> 6] = pc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int c = 0;
-    for (int w = 0; w < NT / 64; ++w) c += itmp[w];
-    count[row] = c;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// The same per-row selection with one wave per row (nb <= 2048), no LDS sort
-// and no workgroup barriers: element e = lane * KPL + r of the row lives in
-// register r of lane `lane`, and the bitonic network compares in registers for
-// strides below KPL and across lanes (shuffles) above.  Same keys, so the same
-// order; the float32 sums run in another order than the workgroup version.
-// ---------------------------------------------------------------------------
-template <int NBP>
-__global__ __launch_bounds__(256) void select_wave_kernel(Geo g, float* __restrict__ score,
-                                                          uint32_t* __restrict__ bitmap,
-                                                          int* __restrict__ count, float p,
-                                                          int k_floor, int write_prob) {
-  constexpr int KPL = NBP / 64;   // keys per lane
-  static_assert(KPL >= 1 && KPL <= 32, "one wave per row up to 2048 blocks");
-  __shared__ uint32_t bits[4][NBP / 32 > 1 ? NBP / 32 : 1];
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + wv;
-  if (row >= g.rows) return;   // whole wave: no workgroup barrier below
-  const int nb = g.nb;
-  const int i = row % nb;
-  float* srow = score + (long)row * nb;
-  float sv[KPL];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int r = 0; r < KPL; ++r) {
-    const int j = lane * KPL + r;
-    sv[r] = j < nb ? srow[j] : -INFINITY;
-    mx = fmaxf(mx, sv[r]);
-  }
-  mx = wave_max(mx);
-  float part = 0.f;
-#pragma unroll
-  for (int r = 0; r < KPL; ++r) {
-    const int j = lane * KPL + r;
-    sv[r] = j < nb ? expf(sv[r] - mx) : 0.f;
-    part += sv[r];
-  }
-  const float z = wave_sum(part);
-  unsigned long long key[KPL];
-#pragma unroll
-  for (int r = 0; r < KPL; ++r) {
-    const int j = lane * KPL + r;
-    key[r] = ~0ull;
-    if (j < nb) {
-      const float pj = sv[r] / z;
-      if (write_prob) srow[j] = pj;
-      key[r] = ((unsigned long long)(~__float_as_uint(pj)) << 32) | (unsigned)j;
-    }
-  }
-  // bitonic sort, ascending keys = P descending then index ascending
-#pragma unroll
-  for (int size = 2; size <= NBP; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride >= KPL) {
-        const int ls = stride / KPL;
-#pragma unroll
-        for (int r = 0; r < KPL; ++r) {
-          const unsigned long long o = __shfl_xor(key[r], ls);
-          const int e = lane * KPL + r;
-          const bool lower = (e & stride) == 0, up = (e & size) == 0;
-          const unsigned long long lo = key[r] < o ? key[r] : o, hi = key[r] < o ? o : key[r];
-          key[r] = (lower == up) ? lo : hi;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < KPL; ++r) {
-          if (r & stride) continue;
-          const int e = lane * KPL + r;
-          const bool up = (e & size) == 0;
-          const unsigned long long a = key[r], c = key[r + stride];
-          if ((a > c) == up) { key[r] = c; key[r + stride] = a; }
+        for (int r = 0; r < RPW; ++r) {
+          const float4 qv = Qr[r][d4];
+          acc[r] = fmaf(qv.x, kv.x, acc[r]);
+          acc[r] = fmaf(qv.y, kv.y, acc[r]);
+          acc[r] = fmaf(qv.z, kv.z, acc[r]);
+          acc[r] = fmaf(qv.w, kv.w, acc[r]);
         }
       }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+        key[r][c] = __float_as_int(c * 64 + lane < nb ? acc[r] * scale : -INFINITY);
+    } else {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) key[r][c] = __float_as_int(-INFINITY);
     }
   }
-  // inclusive scan of the sorted masses; first position reaching p
-  float loc[KPL];
-  float run = 0.f;
+
+  // softmax over the row's nb blocks; keys become the bit patterns of P
+  float total[RPW];
 #pragma unroll
-  for (int r = 0; r < KPL; ++r) {
-    const int e = lane * KPL + r;
-    run += (e < nb) ? __uint_as_float(~(uint32_t)(key[r] >> 32)) : 0.f;
-    loc[r] = run;
+  for (int r = 0; r < RPW; ++r) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < KPL; ++c) mx = fmaxf(mx, __int_as_float(key[r][c]));
+    mx = wave_max_dpp(mx);
+    float part = 0.f;
+#pragma unroll
+    for (int c = 0; c < KPL; ++c) {
+      const float e = c < nch ? expf(__int_as_float(key[r][c]) - mx) : 0.f;
+      key[r][c] = __float_as_int(e);
+      part += e;
+    }
+    const float z = wave_sum_dpp(part);
+    const int row = bh * nb + i0 + r;
+    const bool live = i0 + r < nb;
+    part = 0.f;
+#pragma unroll
+    for (int c = 0; c < KPL; ++c) {
+      const int j = c * 64 + lane;
+      const float pj = __int_as_float(key[r][c]) / z;
+      if (prob && live && j < nb) prob[(long)row * nb + j] = pj;
+      key[r][c] = j < nb ? __float_as_int(pj) : -1;
+      part += j < nb ? pj : 0.f;
+    }
+    total[r] = wave_sum_dpp(part);
   }
-  const float pre = wave_inclusive_scan(run) - run;
-  int first = nb;
+
+  // mass bisection, the wave's rows in lockstep
+  int lo[RPW], hi[RPW];
+  float shi[RPW];
 #pragma unroll
-  for (int r = KPL - 1; r >= 0; --r) {
-    const int e = lane * KPL + r;
-    if (e < nb && pre + loc[r] >= p) first = e + 1;
-  }
+  for (int r = 0; r < RPW; ++r) { lo[r] = 0; hi[r] = 0x3f800001; shi[r] = 0.f; }
+  for (int step = 0; step < 30; ++step) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o));
-  const int m = (p >= 1.0f) ? nb : first;
-  const int m2 = min(nb, max(m, k_floor));
-  uint32_t* wb = bits[wv];
-  for (int w = lane; w < NBP / 32; w += 64) wb[w] = 0u;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
+    for (int r = 0; r < RPW; ++r) {
+      const int mid = lo[r] + ((hi[r] - lo[r]) >> 1);
+      float part = 0.f;
 #pragma unroll
-  for (int r = 0; r < KPL; ++r) {
-    const int e = lane * KPL + r;
-    if (e < m2) {
-      const int j = (int)(key[r] & 0xffffffffu);
-      atomicOr(&wb[j >> 5], 1u << (j & 31));
+      for (int c = 0; c < KPL; ++c)
+        if (c < nch) part += key[r][c] >= mid ? __int_as_float(key[r][c]) : 0.f;
+      const float sm = wave_sum_dpp(part);
+      if (sm >= p) lo[r] = mid;
+      else { hi[r] = mid; shi[r] = sm; }
     }
   }
-  if (lane == 0) atomicOr(&wb[i >> 5], 1u << (i & 31));
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  int pc = 0;
-  for (int w = lane; w < g.words; w += 64) {
-    const uint32_t v = wb[w];
-    bitmap[(long)row * g.words + w] = v;
-    pc += __popc(v);
+
+  int mine = 0;   // kept blocks of this wave's live rows
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int i = i0 + r;
+    if (i >= nb) continue;   // wave-uniform
+    const int row = bh * nb + i;
+    int thr, ktie;           // keep key > thr, and the first ktie blocks with key == thr
+    if (p >= 1.0f || !(total[r] >= p)) {
+      thr = -1; ktie = 0;    // every block (p = 1, or rounding left the total below p)
+    } else {
+      int cg = 0, ct = 0;
+#pragma unroll
+      for (int c = 0; c < KPL; ++c)
+        if (c < nch) {
+          cg += popc_ballot(key[r][c] > lo[r]);
+          ct += popc_ballot(key[r][c] == lo[r]);
+        }
+      const float v = __int_as_float(lo[r]);
+      int need = ct;
+      if (v > 0.f) {
+        const float t = ceilf((p - shi[r]) / v);
+        need = t < 1.f ? 1 : (t < (float)ct ? (int)t : ct);
+      }
+      const int m = cg + need;
+      const int m2 = min(nb, max(m, k_floor));
+      if (m2 >= nb) {
+        thr = -1; ktie = 0;
+      } else if (m2 == m) {
+        thr = lo[r]; ktie = need;
+      } else {
+        // floor: the largest t with at least m2 blocks at or above it
+        int a = 0, bnd = 0x3f800001;
+        for (int step = 0; step < 30; ++step) {
+          const int mid = a + ((bnd - a) >> 1);
+          int cnt = 0;
+#pragma unroll
+          for (int c = 0; c < KPL; ++c)
+            if (c < nch) cnt += popc_ballot(key[r][c] >= mid);
+          if (cnt >= m2) a = mid;
+          else bnd = mid;
+        }
+        int above = 0;
+#pragma unroll
+        for (int c = 0; c < KPL; ++c)
+          if (c < nch) above += popc_ballot(key[r][c] > a);
+        thr = a; ktie = m2 - above;
+      }
+    }
+    int kept = 0, tie_seen = 0;
+#pragma unroll
+    for (int c = 0; c < KPL; ++c) {
+      if (c >= nch) continue;
+      const int j = c * 64 + lane;
+      const bool eq = key[r][c] == thr && thr >= 0;
+      const unsigned long long em = __ballot(eq);
+      const int rank = tie_seen + __popcll(em & ((1ull << lane) - 1ull));
+      tie_seen += __popcll(em);
+      const bool keep = j < nb && (key[r][c] > thr || (eq && rank < ktie) || j == i);
+      const unsigned long long km = __ballot(keep);
+      kept += __popcll(km);
+      uint32_t* wp = bitmap + (long)row * g.words + 2 * c;
+      if (lane == 0) wp[0] = (uint32_t)km;
+      if (lane == 1 && 2 * c + 1 < g.words) wp[1] = (uint32_t)(km >> 32);
+    }
+    if (lane == 0) count[row] = kept;
+    mine += kept;
   }
-  pc = wave_sum_int(pc);
-  if (lane == 0) count[row] = pc;
+  if (lane == 0) wsum[wv] = mine;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    gsum[bh * gridDim.x + blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
 }
 
 // ---------------------------------------------------------------------------
@@ -627,52 +867,73 @@ __global__ __launch_bounds__(256) void slack_budget_kernel(const long long* __re
 }
 
 // ---------------------------------------------------------------------------
-// CSR: exclusive scan of the row counts (one workgroup), then per-row
-// emission of ascending column indices from the bitmap (one wave per row).
+// Kept blocks per row group (one thread per group), after a slack fill has
+// changed the row counts.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void csr_scan_kernel(Geo g, const int* __restrict__ count,
-                                                        int* __restrict__ row_ptr,
-                                                        int* __restrict__ head_nnz) {
-  __shared__ int itmp[17];
-  constexpr int PER = 8;
-  int carry = 0;
-  for (int base = 0; base < g.rows; base += 1024 * PER) {
-    const int r0 = base + threadIdx.x * PER;
-    int v[PER];
-    int run = 0;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      v[e] = (r0 + e < g.rows) ? count[r0 + e] : 0;
-      run += v[e];
-    }
-    int tot;
-    int ex = block_exclusive_scan<1024>(run, itmp, &tot) + carry;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      if (r0 + e < g.rows) row_ptr[r0 + e] = ex;
-      ex += v[e];
-    }
-    carry += tot;
-  }
-  if (threadIdx.x == 0) row_ptr[g.rows] = carry;
-  __syncthreads();
-  for (int bh = threadIdx.x; bh < g.B * g.H; bh += 1024)
-    head_nnz[bh] = row_ptr[(bh + 1) * g.nb] - row_ptr[bh * g.nb];
+__global__ __launch_bounds__(256) void route_gsum_kernel(Geo g, const int* __restrict__ count,
+                                                         int* __restrict__ gsum, int rpg,
+                                                         int gph) {
+  const int x = blockIdx.x * 256 + threadIdx.x;
+  if (x >= g.B * g.H * gph) return;
+  const int bh = x / gph, i0 = (x % gph) * rpg;
+  int s = 0;
+  for (int i = i0; i < min(g.nb, i0 + rpg); ++i) s += count[bh * g.nb + i];
+  gsum[x] = s;
 }
 
-__global__ __launch_bounds__(256) void csr_emit_kernel(Geo g, const uint32_t* __restrict__ bitmap,
-                                                       const int* __restrict__ row_ptr,
-                                                       int* __restrict__ col_idx) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= g.rows) return;
-  int* out = col_idx + row_ptr[row];
-  for (int c0 = 0; c0 < g.nb; c0 += 64) {
-    const int j = c0 + lane;
-    const bool bit = j < g.nb && ((bitmap[(long)row * g.words + (j >> 5)] >> (j & 31)) & 1u);
-    const unsigned long long m = __ballot(bit);
-    if (bit) out[__popcll(m & ((1ull << lane) - 1ull))] = j;
-    out += __popcll(m);
+// ---------------------------------------------------------------------------
+// CSR over the row groups of route_select_kernel (same grid): a group's first
+// position is the sum of the totals of all groups before it (read from gsum),
+// its rows follow in order, and each row's columns are its bitmap's set bits
+// in ascending order (one wave per row, 64 columns per ballot).  The first
+// group of a head also writes the head's total, the last group the end of
+// row_ptr.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void route_csr_kernel(Geo g, const uint32_t* __restrict__ bitmap,
+                                                        const int* __restrict__ count,
+                                                        const int* __restrict__ gsum, int rpg,
+                                                        int* __restrict__ row_ptr,
+                                                        int* __restrict__ col_idx,
+                                                        int* __restrict__ head_nnz) {
+  __shared__ int tmp[8];
+  __shared__ int roff[17];
+  const int bh = blockIdx.y, x = blockIdx.x, gph = gridDim.x;
+  const int lin = bh * gph + x;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int a = 0, hs = 0;
+  for (int w = threadIdx.x; w < lin; w += 256) a += gsum[w];
+  if (x == 0)
+    for (int w = threadIdx.x; w < gph; w += 256) hs += gsum[bh * gph + w];
+  a = wave_sum_int(a);
+  hs = wave_sum_int(hs);
+  if (lane == 0) { tmp[wv] = a; tmp[4 + wv] = hs; }
+  const int i0 = x * rpg, n = min(rpg, g.nb - i0);
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int r = 0; r < n; ++r) {
+      roff[r] = run;
+      run += count[bh * g.nb + i0 + r];
+    }
+    roff[n] = run;
+  }
+  __syncthreads();
+  const int base = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  if (threadIdx.x == 0) {
+    if (x == 0) head_nnz[bh] = tmp[4] + tmp[5] + tmp[6] + tmp[7];
+    if (lin == g.B * g.H * gph - 1) row_ptr[g.rows] = base + roff[n];
+  }
+  for (int r = wv; r < n; r += 4) {
+    const int row = bh * g.nb + i0 + r;
+    const int start = base + roff[r];
+    if (lane == 0) row_ptr[row] = start;
+    int* out = col_idx + start;
+    for (int c0 = 0; c0 < g.nb; c0 += 64) {
+      const int j = c0 + lane;
+      const bool bit = j < g.nb && ((bitmap[(long)row * g.words + (j >> 5)] >> (j & 31)) & 1u);
+      const unsigned long long m = __ballot(bit);
+      if (bit) out[__popcll(m & ((1ull << lane) - 1ull))] = j;
+      out += __popcll(m);
+    }
   }
 }
 
@@ -680,60 +941,98 @@ __global__ __launch_bounds__(256) void csr_emit_kernel(Geo g, const uint32_t* __
 template <typename T>
 static void launch_pool(const Geo& g, const void* q, const void* k, float* qp, float* kp,
                         hipStream_t s) {
-  dim3 grid(g.nb, g.B * g.H);
+  // widest head group (at most 8 heads) that divides H, fits 256 chunks and
+  // still gives at least 4096 workgroups (480p: 2 heads, 6160 workgroups; 1,
+  // 2, 4 and 8 heads measured 138, 133, 136 and 141 us there)
+  const int chunks_per_head = g.d * (int)sizeof(T) / 16;
+  int hg = 8;
+  while (hg > 1 && (g.H % hg != 0 || hg * chunks_per_head > 256 ||
+                    (long)g.B * (g.H / hg) * g.nb < 4096))
+    hg /= 2;
+  dim3 grid(g.B * (g.H / hg), g.nb);
   if (g.d == 128)
     hipLaunchKernelGGL((pool_kernel<T, 128>), grid, dim3(256), 0, s, g, (const T*)q,
-                       (const T*)k, qp, kp);
+                       (const T*)k, qp, kp, hg);
   else
     hipLaunchKernelGGL((pool_kernel<T, 64>), grid, dim3(256), 0, s, g, (const T*)q,
-                       (const T*)k, qp, kp);
+                       (const T*)k, qp, kp, hg);
 }
 
-template <int NBP>
-static void launch_select_n(const Geo& g, float* score, uint32_t* bm, int* cnt, float p,
-                            int kf, int wp, hipStream_t s) {
-  hipLaunchKernelGGL((select_kernel<NBP>), dim3(g.rows), dim3(256), 0, s, g, score, bm, cnt, p,
-                     kf, wp);
+template <int D, int KPL>
+static void launch_select_wide(const Geo& g, dim3 grid, const float* qp, const float* kp,
+                               uint32_t* bm, int* cnt, int* gsum, float* prob, float p, int kf,
+                               float scale, hipStream_t s) {
+  hipLaunchKernelGGL((route_select_wide_kernel<D, KPL, 1>), grid, dim3(256), 0, s, g, qp, kp, bm,
+                     cnt, gsum, prob, p, kf, scale);
 }
 
-template <int NBP>
-static void launch_select_wave(const Geo& g, float* score, uint32_t* bm, int* cnt, float p,
-                               int kf, int wp, hipStream_t s) {
-  hipLaunchKernelGGL((select_wave_kernel<NBP>), dim3((g.rows + 3) / 4), dim3(256), 0, s, g, score,
-                     bm, cnt, p, kf, wp);
+template <int D, int NC>
+static void launch_select16(const Geo& g, dim3 grid, const float* qp, const float* kp,
+                            uint32_t* bm, int* cnt, int* gsum, float* prob, float p, int kf,
+                            float scale, hipStream_t s) {
+  hipLaunchKernelGGL((route_select_kernel<D, NC>), grid, dim3(256), 0, s, g, qp, kp, bm, cnt, gsum,
+                     prob, p, kf, scale);
 }
 
-static void launch_select(const Geo& g, float* score, uint32_t* bm, int* cnt, float p, int kf,
-                          int wp, hipStream_t s) {
-  if (g.nb <= 64) launch_select_wave<64>(g, score, bm, cnt, p, kf, wp, s);
-  else if (g.nb <= 128) launch_select_wave<128>(g, score, bm, cnt, p, kf, wp, s);
-  else if (g.nb <= 256) launch_select_wave<256>(g, score, bm, cnt, p, kf, wp, s);
-  else if (g.nb <= 512) launch_select_wave<512>(g, score, bm, cnt, p, kf, wp, s);
-  else if (g.nb <= 1024) launch_select_wave<1024>(g, score, bm, cnt, p, kf, wp, s);
-  else if (g.nb <= 2048) launch_select_wave<2048>(g, score, bm, cnt, p, kf, wp, s);
-  else launch_select_n<4096>(g, score, bm, cnt, p, kf, wp, s);
+template <int D>
+static void launch_select_d(const Geo& g, dim3 grid, const float* qp, const float* kp,
+                            uint32_t* bm, int* cnt, int* gsum, float* prob, float p, int kf,
+                            float scale, hipStream_t s) {
+  const int nch = (g.nb + 63) / 64;
+#define ABS_SEL16(NC_)                                                                   \
+  if (nch <= NC_) {                                                                      \
+    launch_select16<D, NC_>(g, grid, qp, kp, bm, cnt, gsum, prob, p, kf, scale, s);      \
+    return;                                                                              \
+  }
+  ABS_SEL16(1) ABS_SEL16(2) ABS_SEL16(3) ABS_SEL16(4) ABS_SEL16(5) ABS_SEL16(6)
+  ABS_SEL16(8) ABS_SEL16(10) ABS_SEL16(12) ABS_SEL16(16)
+#undef ABS_SEL16
+  if (nch <= 32) launch_select_wide<D, 32>(g, grid, qp, kp, bm, cnt, gsum, prob, p, kf, scale, s);
+  else launch_select_wide<D, 64>(g, grid, qp, kp, bm, cnt, gsum, prob, p, kf, scale, s);
+}
+
+// pooling, then scores + softmax + selection (P kept for a slack fill when
+// `prob` is given)
+static void launch_route_front(const Geo& g, int dtype, const void* q, const void* k, float p,
+                               int k_floor, char* ws, const RouteWs& L, float* prob,
+                               hipStream_t s) {
+  float* qp = (float*)(ws + L.qp);
+  float* kp = (float*)(ws + L.kp);
+  if (dtype == ABS_BF16) launch_pool<bf16_t>(g, q, k, qp, kp, s);
+  else launch_pool<float>(g, q, k, qp, kp, s);
+  static_assert(MAX_NB <= 64 * 64, "one wave's registers hold a row of at most 4096 blocks");
+  const dim3 grid(route_groups_per_head(g.nb), g.B * g.H);
+  const float scale = (float)(1.0 / sqrt((double)g.d));
+  uint32_t* bm = (uint32_t*)(ws + L.bitmap);
+  int* cnt = (int*)(ws + L.count);
+  int* gsum = (int*)(ws + L.gsum);
+  if (g.d == 128) launch_select_d<128>(g, grid, qp, kp, bm, cnt, gsum, prob, p, k_floor, scale, s);
+  else launch_select_d<64>(g, grid, qp, kp, bm, cnt, gsum, prob, p, k_floor, scale, s);
+}
+
+static void launch_route_csr(const Geo& g, char* ws, const RouteWs& L, bool recount,
+                             const abs_mask* mask, hipStream_t s) {
+  const int rpg = route_group_rows(g.nb), gph = route_groups_per_head(g.nb);
+  int* cnt = (int*)(ws + L.count);
+  int* gsum = (int*)(ws + L.gsum);
+  if (recount) {
+    const int groups = g.B * g.H * gph;
+    hipLaunchKernelGGL(route_gsum_kernel, dim3((groups + 255) / 256), dim3(256), 0, s, g, cnt,
+                       gsum, rpg, gph);
+  }
+  hipLaunchKernelGGL(route_csr_kernel, dim3(gph, g.B * g.H), dim3(256), 0, s, g,
+                     (const uint32_t*)(ws + L.bitmap), cnt, gsum, rpg, mask->row_ptr,
+                     mask->col_idx, mask->head_nnz);
 }
 
 hipError_t launch_route(const Geo& g, int dtype, const void* q, const void* k, float p,
                         int k_floor, float slack, const abs_mask* mask, char* ws,
                         const RouteWs& L, hipStream_t s) {
-  float* qp = (float*)(ws + L.qp);
-  float* kp = (float*)(ws + L.kp);
-  float* score = (float*)(ws + L.score);
+  const bool do_slack = slack > 0.f;
+  float* prob = do_slack ? (float*)(ws + L.prob) : nullptr;
+  launch_route_front(g, dtype, q, k, p, k_floor, ws, L, prob, s);
   uint32_t* bm = (uint32_t*)(ws + L.bitmap);
   int* cnt = (int*)(ws + L.count);
-  if (dtype == ABS_BF16) launch_pool<bf16_t>(g, q, k, qp, kp, s);
-  else launch_pool<float>(g, q, k, qp, kp, s);
-  {
-    dim3 grid((g.nb + 63) / 64, (g.nb + 63) / 64, g.B * g.H);
-    const float scale = (float)(1.0 / sqrt((double)g.d));
-    if (g.d == 128)
-      hipLaunchKernelGGL(scores_kernel<128>, grid, dim3(256), 0, s, g, qp, kp, score, scale);
-    else
-      hipLaunchKernelGGL(scores_kernel<64>, grid, dim3(256), 0, s, g, qp, kp, score, scale);
-  }
-  const bool do_slack = slack > 0.f;
-  launch_select(g, score, bm, cnt, p, k_floor, do_slack ? 1 : 0, s);
   if (do_slack) {
     const long long budget = (long long)ceil((double)slack * (double)g.nb * (double)g.nb);
     uint32_t* hist = (uint32_t*)(ws + L.hist);
@@ -745,42 +1044,27 @@ hipError_t launch_route(const Geo& g, int dtype, const void* q, const void* k, f
     const int rpw = 8;
     for (int pass = 0; pass < 3; ++pass) {
       hipLaunchKernelGGL(slack_hist_kernel, dim3((g.nb + rpw - 1) / rpw, heads), dim3(256), 0, s,
-                         g, score, bm, sel, hist, pass, rpw, g.nb, 0.0f);
+                         g, prob, bm, sel, hist, pass, rpw, g.nb, 0.0f);
       hipLaunchKernelGGL(slack_pick_kernel, dim3(heads), dim3(256), 0, s, sel, hist, pass);
     }
     const int wg4 = (g.rows + 3) / 4;
-    hipLaunchKernelGGL(slack_eqcount_kernel, dim3(wg4), dim3(256), 0, s, g, score, bm, sel, eqcnt,
+    hipLaunchKernelGGL(slack_eqcount_kernel, dim3(wg4), dim3(256), 0, s, g, prob, bm, sel, eqcnt,
                        g.nb, 0.0f);
     hipLaunchKernelGGL(slack_eqscan_kernel, dim3(heads), dim3(256), 0, s, g, eqcnt, eqoff, g.nb);
-    hipLaunchKernelGGL(slack_mark_kernel, dim3(wg4), dim3(256), 0, s, g, score, bm, cnt, sel,
+    hipLaunchKernelGGL(slack_mark_kernel, dim3(wg4), dim3(256), 0, s, g, prob, bm, cnt, sel,
                        eqoff, g.nb, 0.0f);
   }
-  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, s, g, cnt, mask->row_ptr,
-                     mask->head_nnz);
-  hipLaunchKernelGGL(csr_emit_kernel, dim3((g.rows + 3) / 4), dim3(256), 0, s, g, bm,
-                     mask->row_ptr, mask->col_idx);
+  launch_route_csr(g, ws, L, do_slack, mask, s);
   return hipGetLastError();
 }
 
 hipError_t launch_route_dynamic(const Geo& g, int dtype, const void* q, const void* k, float p,
                                 int k_floor, float theta, const long long* budget,
                                 const abs_mask* mask, char* ws, const RouteWs& L, hipStream_t s) {
-  float* qp = (float*)(ws + L.qp);
-  float* kp = (float*)(ws + L.kp);
-  float* score = (float*)(ws + L.score);
+  float* prob = (float*)(ws + L.prob);
+  launch_route_front(g, dtype, q, k, p, k_floor, ws, L, prob, s);
   uint32_t* bm = (uint32_t*)(ws + L.bitmap);
   int* cnt = (int*)(ws + L.count);
-  if (dtype == ABS_BF16) launch_pool<bf16_t>(g, q, k, qp, kp, s);
-  else launch_pool<float>(g, q, k, qp, kp, s);
-  {
-    dim3 grid((g.nb + 63) / 64, (g.nb + 63) / 64, g.B * g.H);
-    const float scale = (float)(1.0 / sqrt((double)g.d));
-    if (g.d == 128)
-      hipLaunchKernelGGL(scores_kernel<128>, grid, dim3(256), 0, s, g, qp, kp, score, scale);
-    else
-      hipLaunchKernelGGL(scores_kernel<64>, grid, dim3(256), 0, s, g, qp, kp, score, scale);
-  }
-  launch_select(g, score, bm, cnt, p, k_floor, 1, s);
   // one group: the whole batch
   uint32_t* hist = (uint32_t*)(ws + L.hist);
   int* sel = (int*)(ws + L.sel);
@@ -790,19 +1074,16 @@ hipError_t launch_route_dynamic(const Geo& g, int dtype, const void* q, const vo
   const int rpw = 64;
   for (int pass = 0; pass < 3; ++pass) {
     hipLaunchKernelGGL(slack_hist_kernel, dim3((g.rows + rpw - 1) / rpw, 1), dim3(256), 0, s, g,
-                       score, bm, sel, hist, pass, rpw, g.rows, theta);
+                       prob, bm, sel, hist, pass, rpw, g.rows, theta);
     hipLaunchKernelGGL(slack_pick_kernel, dim3(1), dim3(256), 0, s, sel, hist, pass);
   }
   const int wg4 = (g.rows + 3) / 4;
-  hipLaunchKernelGGL(slack_eqcount_kernel, dim3(wg4), dim3(256), 0, s, g, score, bm, sel, eqcnt,
+  hipLaunchKernelGGL(slack_eqcount_kernel, dim3(wg4), dim3(256), 0, s, g, prob, bm, sel, eqcnt,
                      g.rows, theta);
   hipLaunchKernelGGL(slack_eqscan_kernel, dim3(1), dim3(256), 0, s, g, eqcnt, eqoff, g.rows);
-  hipLaunchKernelGGL(slack_mark_kernel, dim3(wg4), dim3(256), 0, s, g, score, bm, cnt, sel, eqoff,
+  hipLaunchKernelGGL(slack_mark_kernel, dim3(wg4), dim3(256), 0, s, g, prob, bm, cnt, sel, eqoff,
                      g.rows, theta);
-  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, s, g, cnt, mask->row_ptr,
-                     mask->head_nnz);
-  hipLaunchKernelGGL(csr_emit_kernel, dim3((g.rows + 3) / 4), dim3(256), 0, s, g, bm,
-                     mask->row_ptr, mask->col_idx);
+  launch_route_csr(g, ws, L, true, mask, s);
   return hipGetLastError();
 }
 

@@ -27,6 +27,7 @@ from .abs_oracle import (  # noqa: F401
     dense_attention,
     schedule,
     row_exemptions,
+    row_exemption_causes,
     split_units,
     partial_attention,
     merge_partials,

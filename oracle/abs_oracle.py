@@ -195,24 +195,35 @@ def _select_head(P: np.ndarray, p: float, k_floor: int):
     return keep, diag
 
 
-def row_exemptions(diag: Dict[str, np.ndarray], p: float, k_floor: int,
-                   gap: float = 1e-4, tie_rel: float = 1e-5) -> np.ndarray:
-    """True for rows whose kept set is not decided robustly in float32.
+def row_exemption_causes(diag: Dict[str, np.ndarray], p: float, k_floor: int,
+                         gap: float = 1e-4, tie_rel: float = 1e-5):
+    """The two reasons a row's kept set is not decided robustly in float32,
+    as boolean arrays (close, near_tie):
 
-    A row is exact-checked when its cumulative mass is further than ``gap`` from
-    p on both sides of the cut (or the floor decides the count), and the two
-    probabilities straddling the final cut are not a near tie
-    (0 < |P_cut - P_next| <= tie_rel * P_cut).  Exact ties are not exempt: the
-    lowest-index rule decides them on both sides.
+    close:    the cumulative mass is within ``gap`` of p on one side of the cut
+              (and the floor does not decide the count);
+    near_tie: the two probabilities straddling the final cut are a near tie,
+              0 < |P_cut - P_next| <= tie_rel * P_cut.  Exact ties are not a
+              reason: the lowest-index rule decides them on both sides.
     """
     m = np.asarray(diag["m"])
     if p >= 1.0:
-        return np.zeros(m.shape, dtype=bool)
+        none = np.zeros(m.shape, dtype=bool)
+        return none, none.copy()
     close = np.minimum(np.abs(diag["c_prev"] - p), np.abs(diag["c_at"] - p)) <= gap
     close &= ~(m < k_floor)
     dp = np.abs(diag["p_cut"] - diag["p_next"])
     near_tie = (dp > 0) & (dp <= tie_rel * diag["p_cut"])
     near_tie &= ~np.isnan(diag["p_next"])
+    return close, near_tie
+
+
+def row_exemptions(diag: Dict[str, np.ndarray], p: float, k_floor: int,
+                   gap: float = 1e-4, tie_rel: float = 1e-5) -> np.ndarray:
+    """True for rows whose kept set is not decided robustly in float32: rows
+    with either reason of row_exemption_causes.  Every other row is
+    exact-checked."""
+    close, near_tie = row_exemption_causes(diag, p, k_floor, gap, tie_rel)
     return close | near_tie
 
 

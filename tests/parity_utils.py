@@ -12,19 +12,28 @@ import oracle as O
 TOL_BF16_MAX, TOL_BF16_MEAN, TOL_F32_MAX = 2e-2, 2e-3, 1e-4
 
 
+# At most this fraction of all rows may be exempt rows where the GPU and the
+# oracle keep different sets (float32 deciding a near-threshold row the other
+# way); rows outside the exemption rule may differ nowhere.
+MAX_EXEMPT_DIFFERING = 0.005
+
+
 def compare_masks(gpu_keep: np.ndarray, res: dict, p: float, k_floor: int, key: str = "keep"):
     """Row-by-row comparison of a GPU mask with the oracle's.
 
     Rows outside the float32 exemption rule (oracle.row_exemptions) must match
     exactly.  Exempt rows must keep the own block, at least min(k_floor, nb)
     blocks, mass >= p - 1e-4 (oracle P), a size within 1 of the oracle's and a
-    symmetric difference of at most 2 blocks.
-    Returns a dict of counts; raises AssertionError on any violation.
+    symmetric difference of at most 2 blocks; and at most MAX_EXEMPT_DIFFERING
+    of all rows may be exempt rows that differ from the oracle.
+    Returns a dict of counts (exempt rows split by reason: mass within 1e-4 of
+    p, near tie at the cut); raises AssertionError on any violation.
     """
     ref = res[key]
     B, H, nb, _ = ref.shape
     P = res["P"]
-    exempt = O.row_exemptions(res["diag"], p, k_floor)
+    close, near_tie = O.row_exemption_causes(res["diag"], p, k_floor)
+    exempt = close | near_tie
     exact_rows = mism = ex_ok = ex_equal = 0
     bad = []
     for b in range(B):
@@ -50,7 +59,12 @@ def compare_masks(gpu_keep: np.ndarray, res: dict, p: float, k_floor: int, key: 
                 ex_ok += 1
                 ex_equal += int(eq[i])
     assert mism == 0, f"{mism} non-exempt rows differ, e.g. {bad}"
-    return dict(exact=exact_rows, exempt=ex_ok, exempt_but_equal=ex_equal, mismatched=mism)
+    rows = B * H * nb
+    differing = ex_ok - ex_equal
+    assert differing <= MAX_EXEMPT_DIFFERING * rows, (differing, rows)
+    return dict(exact=exact_rows, exempt=ex_ok, exempt_mass_close=int(close.sum()),
+                exempt_near_tie=int((near_tie & ~close).sum()), exempt_but_equal=ex_equal,
+                exempt_differing=differing, mismatched=mism)
 
 
 def check_slack(gpu_keep: np.ndarray, gpu_base: np.ndarray, P: np.ndarray, slack: float,
