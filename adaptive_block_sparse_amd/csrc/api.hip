@@ -6,6 +6,7 @@
 
 #include "abs.h"
 #include "internal.h"
+#include "route_internal.h"
 
 namespace abs_impl {
 

@@ -8,6 +8,7 @@
 
 #include "abs.h"
 #include "internal.h"
+#include "route_internal.h"
 
 // The workspace of abs_route_noalloc.  Each GPU the library runs on holds its
 // own copy until the process ends.  In host code this name is only a stand-in

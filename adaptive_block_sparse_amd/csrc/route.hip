@@ -10,6 +10,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "route_internal.h"
 
 namespace abs_impl {
 

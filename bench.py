@@ -85,6 +85,70 @@ def measured_traffic(workload_cfg: int, sched: str):
     return int(fields["traffic_bytes_per_launch"])
 
 
+def _profile_fields(name: str):
+    path = os.path.join(ROOT, "profiles", name)
+    fields = {}
+    if os.path.exists(path):
+        for line in open(path):
+            if ":" in line and not line.startswith((" ", "|", "#", "*")):
+                key, _, val = line.partition(":")
+                fields[key.strip()] = val.strip()
+    return fields
+
+
+def measured_executed_flop(workload_cfg: int, sched: str):
+    """bf16 MFMA flop executed per launch of the attention kernel, from the
+    committed rocprofv3 SQ_INSTS_VALU_MFMA_MOPS_BF16 summary, if it was taken
+    on this workload and launch and the kernel code has not changed since
+    (else None)."""
+    if workload_cfg != 1:
+        return None
+    f = _profile_fields("attn_bf16_wan22_480p_mfma_lds_counters.md")
+    if (f.get("attend_code_sha256") != code_digest(*ATTEND_SOURCES) or f.get("sched") != sched
+            or "executed_flop_per_launch" not in f):
+        return None
+    return float(f["executed_flop_per_launch"])
+
+
+def cpu_description():
+    """CPU model, the cores this process may run on, and the BLAS threads."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    affinity = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max(int(i.get("num_threads", 1)) for i in threadpool_info()) or 1
+    except Exception:
+        blas = affinity
+    return {"cpu_model": model, "affinity_cores": affinity, "blas_threads": blas}
+
+
+def mask_parity_counts(res: dict, p: float, k_floor: int, rp, ci):
+    """The GPU mask against the oracle's, row by row (counts only; the GPU
+    tests assert): rows the float32 exemption rule leaves exact-checked and
+    whether they match, and exempt rows by reason and whether they match."""
+    import oracle as O
+    B, H, nb, _ = res["base_keep"].shape
+    keep = O.csr_to_keep(rp, ci, B, H, nb)
+    ref = res["keep"]
+    same = (keep == ref).all(axis=-1)
+    close, near = O.row_exemption_causes(res["diag"], p, k_floor)
+    exempt = close | near
+    return {"rows": int(same.size),
+            "exact_checked_equal": int((same & ~exempt).sum()),
+            "exact_checked_differing": int((~same & ~exempt).sum()),
+            "exempt_mass_close": int(close.sum()),
+            "exempt_near_tie": int((near & ~close).sum()),
+            "exempt_equal": int((same & exempt).sum()),
+            "exempt_differing": int((~same & exempt).sum())}
+
+
 def block_valid_counts(grid, block) -> np.ndarray:
     """Real tokens in each 3D block (row-major block order)."""
     per_axis = []
@@ -142,15 +206,11 @@ def cpu_baseline(wl, p, inputs, rp, ci, budget_s=20.0):
     """The oracle, as it stands, on the host cores: full routing of every row,
     attention on a seeded row sample extrapolated by kept tiles."""
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) or 1
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    cpu = cpu_description()
     q, k, v = (t.float().numpy() for t in inputs)
     geo = O.geometry(wl.grid, wl.block)
     t0 = time.perf_counter()
-    O.route(q, k, geo, p, wl.k_floor, wl.slack)
+    res = O.route(q, k, geo, p, wl.k_floor, wl.slack)
     t_route = time.perf_counter() - t0
     counts = np.diff(rp)
     rng = np.random.default_rng(7)
@@ -167,7 +227,7 @@ def cpu_baseline(wl, p, inputs, rp, ci, budget_s=20.0):
     total_tiles = int(counts.sum())
     t_layer = t_route + t_att * total_tiles / done_tiles
     return dict(t_layer_s=t_layer, t_route_s=t_route, rows=done_rows, tiles=done_tiles,
-                total_tiles=total_tiles, cores=threads)
+                total_tiles=total_tiles, cores=cpu["blas_threads"], cpu=cpu, route=res)
 
 
 def main():
@@ -197,9 +257,13 @@ def main():
                     help="score threshold of the dynamic fill (P >= theta)")
     ap.add_argument("--slack-cap", type=int, default=None,
                     help="cap on pairs the dynamic fill adds (default: 5%% of the base mask)")
+    ap.add_argument("--pipeline", default="beside_route",
+                    choices=["beside_route", "after_route", "serial"],
+                    help="where the mask-independent K/V re-layout runs: on a second stream "
+                         "beside routing (default); on a second stream after routing, beside "
+                         "the mask-dependent schedule; or after routing on one stream")
     ap.add_argument("--no-overlap", action="store_true",
-                    help="run the K/V re-layout after routing on one stream instead of "
-                         "beside it on a second stream")
+                    help="the same as --pipeline serial")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--timed-only", action="store_true",
                     help="run only the warmup and timed steps (no schedule sweep, cold step or "
@@ -311,16 +375,20 @@ def main():
                "base_busy_max_over_mean": round(imbalance(
                    tel0.cpu().numpy().reshape(-1, 4))["busy_max_over_mean"], 4)}
 
-    # the K/V re-layout does not depend on the mask: it runs on a second stream
-    # (default priority) beside the routing, joined before the schedule
-    overlap = not split and not args.no_overlap
+    # The K/V re-layout does not depend on the mask, so it can run on a second
+    # stream (default priority).  Beside routing (the default), routing and the
+    # re-layout share HBM bandwidth: the routing kernels take longer, but the
+    # two finish sooner than one after the other (480p, same box: 0.45 against
+    # 0.47 ms from the step's start to the attention launch, either the
+    # re-layout beside the schedule kernels or everything on one stream).
+    pipeline = "serial" if (split or args.no_overlap) else args.pipeline
     side = torch.cuda.Stream(device=dev)
     fork, join = torch.cuda.Event(), torch.cuda.Event()
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        if overlap:
+        if pipeline == "beside_route":
             fork.record(stream)            # after the previous step's attention
             side.wait_event(fork)
             A.attend_relayout(plan, k, v, aws, stream=side)
@@ -332,7 +400,14 @@ def main():
             A.route(plan, q, k, p, wl.k_floor, wl.slack, mask=mask, ws=rws)
         if ev is not None:
             ev[1].record(stream)
-        if overlap:
+        if pipeline == "after_route":
+            fork.record(stream)            # after routing
+            side.wait_event(fork)
+            A.attend_relayout(plan, k, v, aws, stream=side)
+            join.record(side)
+            A.attend_schedule(plan, mask, sched, aws)
+            stream.wait_event(join)
+        elif pipeline == "beside_route":
             stream.wait_event(join)
             A.attend_schedule(plan, mask, sched, aws)
         else:
@@ -357,9 +432,28 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
+    ms_step_median = float(np.median([e[0].elapsed_time(e[3]) for e in evs]))
     t_route = np.mean([e[0].elapsed_time(e[1]) for e in evs])
     t_prep = np.mean([e[1].elapsed_time(e[2]) for e in evs])
     t_attn = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+
+    # routing on its own (nothing beside it on the GPU): median of 20 launches
+    route_alone = []
+    rmask = A.Mask(plan, dev)
+    for i in range(23):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        if dyn is not None:
+            A.route_dynamic(plan, q, k, p, wl.k_floor, args.slack_theta, budget_t, mask=rmask,
+                            ws=rws)
+        else:
+            A.route(plan, q, k, p, wl.k_floor, wl.slack, mask=rmask, ws=rws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 3:
+            route_alone.append(e0.elapsed_time(e1))
+    del rmask
+    t_route_alone = float(np.median(route_alone))
 
     rp, ci = mask.to_host()
     nnz = int(rp[-1])
@@ -425,10 +519,11 @@ def main():
         bal[name]["xcds_seen"] = int(len(set((t[:, 1] & 0xF).tolist())))
     prepare(mask, sched)   # restore the timed schedule
 
-    # cold step: L2 and Infinity Cache flushed by writing 512 MB first
+    # cold steps: L2 and Infinity Cache flushed by writing 512 MB before each;
+    # the median of 20
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     cold = []
-    for _ in range(0 if args.timed_only else 3):
+    for _ in range(0 if args.timed_only else 20):
         flush.fill_(1)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         step(ev)
@@ -463,11 +558,14 @@ def main():
     probe = mfma_probe(dev) if (not args.timed_only and wl.dtype == "bf16") else None
 
     cpu = None
+    parity = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cb = cpu_baseline(wl, p, inputs, rp, ci)
+        if dyn is None:
+            parity = mask_parity_counts(cb["route"], p, wl.k_floor, rp, ci)
         cpu = {"value": flops / cb["t_layer_s"] / 1e12, "unit": "TFLOP/s (effective, kept blocks)",
-               "cores": cb["cores"], "kind": "oracle",
+               "cores": cb["cores"], "kind": "oracle", **cb["cpu"],
                "sample": (f"full oracle routing of all {rp.size - 1} rows ({cb['t_route_s']:.1f} s) + "
                           f"oracle attention on {cb['rows']} random rows ({cb['tiles']} of "
                           f"{cb['total_tiles']} kept tiles), extrapolated by kept tiles; "
@@ -475,6 +573,8 @@ def main():
                "ms_per_layer": cb["t_layer_s"] * 1e3}
 
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+    executed = None if split else measured_executed_flop(args.workload, args.sched)
+    route_bytes = 2 * wl.tokens * wl.heads * wl.head_dim * (2 if wl.dtype == "bf16" else 4)
     out = {
         "metric": "ms/attn layer + effective TFLOPS (kept blocks) at Wan2.2 480p shape",
         "value": round(eff_layer, 2),
@@ -488,12 +588,14 @@ def main():
                    "p": p, "k_floor": wl.k_floor, "slack": wl.slack, "sched": args.sched,
                    "split": ({"split_tiles": args.split, "max_parts": max_parts} if split
                              else None),
-                   "relayout_beside_route": overlap,
+                   "pipeline": pipeline,
                    "kept_tiles": nnz, "density": round(nnz / (rp.size - 1) / nb, 4),
                    "head_density_min_median_max": [round(float(dens.min()), 4),
                                                    round(float(np.median(dens)), 4),
                                                    round(float(dens.max()), 4)]},
+        "ms_per_step_median": round(ms_step_median, 4),
         "ms_route": round(float(t_route), 4),
+        "ms_route_alone": round(t_route_alone, 4),
         "ms_attend_prepare": round(float(t_prep), 4),
         "ms_attend_kernel": round(float(t_attn), 4),
         "tflops_attend_kernel": round(eff_attn, 2),
@@ -507,11 +609,17 @@ def main():
                                 if args.sched == "head_major"
                                 else "attn_bf16_kernel<128,128,true,false>"),
                      "per_unit": "4*Bt^2*d flop per kept tile",
+                     "frac_valid_pairs": round(valid_flops / (t_attn * 1e-3) / 1e12 / peak, 4),
+                     "frac_executed": (round(executed / (t_attn * 1e-3) / 1e12 / peak, 4)
+                                       if executed else None),
                      "probe_peak": probe["tflops"] if probe else None},
         "mfma_probe_bf16": probe,
-        "route_hbm": {"bytes_read_qk": 2 * wl.tokens * wl.heads * wl.head_dim * 2,
-                      "gbs_algorithmic": round(2 * wl.tokens * wl.heads * wl.head_dim * 2
-                                               / (t_route * 1e-3) / 1e9, 1)},
+        "route_hbm": {"bytes_read_qk": route_bytes,
+                      "gbs_algorithmic_alone": round(route_bytes / (t_route_alone * 1e-3) / 1e9, 1),
+                      "frac_of_8tbs_alone": round(route_bytes / (t_route_alone * 1e-3) / 1e9
+                                                  / PEAK_HBM_GBS, 4),
+                      "gbs_algorithmic_in_step": round(route_bytes / (t_route * 1e-3) / 1e9, 1)},
+        "mask_parity": parity,
         "imbalance": bal,
         "dynamic_slack": dyn,
         "ms_per_step_cold": round(float(np.median(cold)), 4) if cold else None,

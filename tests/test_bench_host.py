@@ -71,3 +71,39 @@ def test_code_digest_ignores_comments_only(tmp_path):
     c.write_text("// header\nint f(int x) {  /* note */\n  return x + 2;   // one\n}\n")
     assert bench.code_digest(str(a)) == bench.code_digest(str(b))
     assert bench.code_digest(str(a)) != bench.code_digest(str(c))
+
+
+def test_cpu_description_names_the_machine():
+    d = bench.cpu_description()
+    assert d["affinity_cores"] == len(os.sched_getaffinity(0)) and d["blas_threads"] >= 1
+    assert d["cpu_model"] is None or isinstance(d["cpu_model"], str)
+
+
+def test_mask_parity_counts_on_the_oracles_own_mask():
+    import oracle as O
+    import synth_inputs as si
+    wl = si.Workload(802, "counts", 1, 2, 64, "f32", (8, 32, 32), (2, 4, 4), (0.9,), 2, 0.0,
+                     "u13")
+    q, k, _ = si.make_inputs(wl)
+    geo = O.geometry(wl.grid, wl.block)
+    p = float(np.float32(0.9))
+    res = O.route(q.numpy(), k.numpy(), geo, p, 2)
+    rp, ci, _ = O.keep_to_csr(res["keep"])
+    c = bench.mask_parity_counts(res, p, 2, rp, ci)
+    assert c["rows"] == 2 * geo.nb
+    assert c["exact_checked_differing"] == 0 and c["exempt_differing"] == 0
+    assert c["exact_checked_equal"] + c["exempt_equal"] == c["rows"]
+    assert c["exempt_mass_close"] + c["exempt_near_tie"] == c["exempt_equal"]
+    # one planted change in an exact-checked row is counted there
+    exempt = O.row_exemptions(res["diag"], p, 2)
+    h, i = map(int, np.argwhere(~exempt[0])[0])
+    keep = res["keep"].copy()
+    j = (i + 1) % geo.nb
+    keep[0, h, i, j] = ~keep[0, h, i, j]
+    rp2, ci2, _ = O.keep_to_csr(keep)
+    assert bench.mask_parity_counts(res, p, 2, rp2, ci2)["exact_checked_differing"] == 1
+
+
+def test_executed_flop_lookup_is_bound_to_workload_and_queue():
+    assert bench.measured_executed_flop(2, "head_phased") is None
+    assert bench.measured_executed_flop(1, "head_major") is None

@@ -348,6 +348,33 @@ def test_full_workload_parity(cfg, p):
         assert np.array_equal(o3.float().cpu().numpy(), r["o"])
 
 
+def test_relayout_after_routing_beside_the_schedule():
+    """abs_attend_relayout on a second stream after abs_route, while
+    abs_attend_schedule runs on the first; the run after an event join gives
+    the same bits as abs_attend on one stream (the benchmark's pipeline)."""
+    wl = SMALL["bf16-d128-bt128-ragged"]
+    inputs = si.make_inputs(wl)
+    want = _run(wl, 0.9, 2, sched=A.SCHED_HEAD_PHASED, inputs=inputs)["o"]
+    q, k, v = (t.to(DEV) for t in inputs)
+    plan = A.plan_init(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.block, wl.dtype)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    ws = A.workspace(plan.attend_ws_bytes, DEV)
+    o = torch.empty_like(q)
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+    for _ in range(2):                       # the second pass reuses the workspace
+        mask = A.route(plan, q, k, 0.9, 2)
+        fork.record(main)
+        side.wait_event(fork)
+        A.attend_relayout(plan, k, v, ws, stream=side)
+        join.record(side)
+        A.attend_schedule(plan, mask, A.SCHED_HEAD_PHASED, ws)
+        main.wait_event(join)
+        A.attend_run(plan, q, k, mask, o, A.SCHED_HEAD_PHASED, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(o.float().cpu().numpy(), want)
+
+
 def test_relayout_beside_routing_on_a_second_stream():
     """abs_attend_relayout on a second stream, overlapping abs_route, then
     abs_attend_schedule and the run after an event join: the same bits as
