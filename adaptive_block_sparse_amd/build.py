@@ -46,6 +46,42 @@ def _compile(lib: str, sources, verbose: bool) -> str:
     return lib
 
 
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer build of the same
+# sources, for the CPU tests of the argument validation paths (device code is
+# built as usual, without sanitizers).  Load it with the sanitizer runtime
+# preloaded (host_sanitizer_env) and ABS_LIBRARY pointing at it.
+SAN_LIB = os.path.join(HERE, "libabs_san.so")
+SAN_FLAGS = ("-O1 -g -Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+             "-Xarch_host -fno-sanitize-recover=undefined "
+             "-Xarch_host -fno-omit-frame-pointer -shared-libsan")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    tmp = SAN_LIB + ".tmp"
+    cmd = [c for c in hipcc_command(tmp) if c != "-O3"]
+    cmd[1:1] = SAN_FLAGS.split()
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
+def host_sanitizer_env() -> dict:
+    """Environment for a process that loads SAN_LIB: the ASan runtime
+    preloaded (the Python interpreter is not instrumented), leak checks off,
+    any report fatal."""
+    asan = subprocess.run(["/opt/rocm/bin/hipcc", "-print-file-name=libclang_rt.asan-x86_64.so"],
+                          capture_output=True, text=True).stdout.strip()
+    env = dict(os.environ)
+    env.update(LD_PRELOAD=asan, ABS_LIBRARY=SAN_LIB,
+               ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    return env
+
+
 def build(verbose: bool = False) -> str:
     _compile(PROBE_LIB, PROBE_SOURCES, verbose)
     return _compile(LIB, SOURCES, verbose)

@@ -237,6 +237,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--p", type=float, default=None)
+    ap.add_argument("--slack", type=float, default=None,
+                    help="per-head slack budget as a fraction of nb^2 (default: the workload's; "
+                         "0 turns the fixed fill off)")
     ap.add_argument("--heads", type=int, default=None,
                     help="run only the first H heads of the workload (one rank's share when "
                          "the layer is sharded by head across GPUs)")
@@ -310,6 +313,11 @@ def main():
             print(f"--heads must be in 1..{wl.heads}", file=sys.stderr)
             sys.exit(2)
         wl = dataclasses.replace(wl, heads=args.heads, name=f"{wl.name}-first{args.heads}heads")
+    if args.slack is not None:
+        if not 0.0 <= args.slack < 1.0:
+            print("--slack must be in [0, 1)", file=sys.stderr)
+            sys.exit(2)
+        wl = dataclasses.replace(wl, slack=args.slack)
     p = float(np.float32(args.p if args.p is not None else wl.p[0]))
     split = args.split is not None
     if split and args.sched not in (None, "nnz_sorted", "head_phased"):
