@@ -31,4 +31,9 @@ from .abs_oracle import (  # noqa: F401
     split_units,
     partial_attention,
     merge_partials,
+    frame_members,
+    frame_pool,
+    select_frames_row,
+    route_frames,
+    sparse_attention_frames,
 )

@@ -363,6 +363,166 @@ def route(Q, K, geo: Geometry, p: float, k_floor: int, slack: float = 0.0):
 
 
 # --------------------------------------------------------------------------
+# Fine-grained Top-p over frames inside the kept blocks
+# --------------------------------------------------------------------------
+def frame_members(geo: Geometry) -> np.ndarray:
+    """[nb, bt, bh*bw] token index of each slot of each frame, -1 for padding.
+
+    A frame is the part of a 3D block at one temporal offset tau: the tokens
+    (t, h, w) of the block with t = (t // bt) * bt + tau.  Slots are row-major
+    with t slowest, so frame tau holds slots [tau*bh*bw, (tau+1)*bh*bw).
+    """
+    bt, bh, bw = geo.block
+    return block_members(geo).reshape(geo.nb, bt, bh * bw)
+
+
+def frame_pool(X, geo: Geometry):
+    """Mean of X over the real tokens of each frame: ([B, H, nb, bt, d], counts
+    [nb, bt]).  A frame with no real token (a block cut along t) has count 0
+    and mean 0."""
+    X = np.asarray(X, dtype=np.float64)
+    B, N, H, d = X.shape
+    fm = frame_members(geo)
+    bt = geo.block[0]
+    out = np.zeros((B, H, geo.nb, bt, d))
+    counts = np.zeros((geo.nb, bt), dtype=np.int64)
+    for j in range(geo.nb):
+        for tau in range(bt):
+            idx = fm[j, tau][fm[j, tau] >= 0]
+            counts[j, tau] = idx.size
+            if idx.size:
+                out[:, :, j, tau, :] = X[:, idx, :, :].mean(axis=1)
+    return out, counts
+
+
+def select_frames_row(scores: np.ndarray, cand: np.ndarray, own: Sequence[int], p_frame: float,
+                      k_floor: int):
+    """Kept frames of one row, as a boolean array over the row's frame index
+    f = j*bt + tau, plus diagnostics.
+
+    Source: FVAttn explainer, "Core method" part 1: Top-p keeps the smallest
+    set whose cumulative similarity mass reaches p, and the video-aware 3D
+    blocks let block-level decisions be combined with Top-p's fine-grained
+    decisions (the fact-check table repeats "block-level decisions combined
+    with fine-grained Top-p").  Reading: after the block-level routing, Top-p
+    runs again over the frames of the row's kept blocks:
+      1. candidates: the frames with real tokens of the kept blocks;
+      2. mass: softmax of the frame scores over the candidates only;
+      3. order by mass, largest first, equal values to the lower frame index;
+      4. m = the smallest count whose cumulative mass reaches p_frame (>=;
+         p_frame >= 1 keeps every candidate; if rounding keeps every partial
+         sum below p_frame, all candidates are kept);
+      5. floor: never fewer than k_floor frames (k_floor beyond the candidate
+         count keeps them all);
+      6. repair: every candidate frame of the own block is kept.
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    cand = np.asarray(cand, dtype=bool)
+    idx = np.nonzero(cand)[0]
+    nc = idx.size
+    z = scores[idx] - scores[idx].max()
+    e = np.exp(z)
+    pc = e / e.sum()
+    order = np.argsort(-pc, kind="stable")        # ties: lower frame index first
+    masses = pc[order]
+    if p_frame >= 1.0:
+        m = nc
+    else:
+        csum = np.cumsum(masses)
+        hit = np.nonzero(csum >= p_frame)[0]
+        m = int(hit[0]) + 1 if hit.size else nc
+    m2 = min(nc, max(m, int(k_floor)))
+    keep = np.zeros(scores.shape[0], dtype=bool)
+    keep[idx[order[:m2]]] = True
+    for f in own:
+        if cand[f]:
+            keep[f] = True
+    csum = np.concatenate([[0.0], np.cumsum(masses)])
+    diag = dict(m=m, m2=m2, c_prev=float(csum[m - 1]), c_at=float(csum[m]),
+                p_cut=float(masses[m2 - 1]),
+                p_next=float(masses[m2]) if m2 < nc else float("nan"))
+    return keep, diag
+
+
+def route_frames(Q, K, geo: Geometry, p: float, k_floor: int, p_frame: float):
+    """Block routing (route, no slack fill) followed by the frame-level Top-p
+    of select_frames_row in every row.  Scores: the query block's mean of Q
+    (as for the blocks) against each frame's mean of K, scale 1/sqrt(d).
+
+    Returns route's dict plus frame_keep [B, H, nb, nb, bt] (kept frames per
+    row and key block), frame_mask (int, aligned with col_idx: bit tau set when
+    frame tau of that kept block is kept) and frame_diag (per-row
+    diagnostics for the exemption rule).
+    """
+    res = route(Q, K, geo, p, k_floor)
+    Kf, counts = frame_pool(K, geo)
+    Qp = res["Qp"]
+    B, H, nb, d = Qp.shape
+    bt = geo.block[0]
+    fkeep = np.zeros((B, H, nb, nb, bt), dtype=bool)
+    diag = {key: np.empty((B, H, nb)) for key in ("m", "m2", "c_prev", "c_at", "p_cut", "p_next")}
+    real = (counts > 0).reshape(-1)
+    for b in range(B):
+        for h in range(H):
+            sc = (np.einsum("id,jtd->ijt", Qp[b, h], Kf[b, h]) / math.sqrt(d)).reshape(nb, nb * bt)
+            for i in range(nb):
+                cand = np.repeat(res["keep"][b, h, i], bt) & real
+                own = range(i * bt, (i + 1) * bt)
+                kf, dg = select_frames_row(sc[i], cand, own, p_frame, k_floor)
+                fkeep[b, h, i] = kf.reshape(nb, bt)
+                for key, val in dg.items():
+                    diag[key][b, h, i] = val
+    rp, ci = res["row_ptr"], res["col_idx"]
+    fmask = np.zeros(ci.size, dtype=np.int64)
+    for r in range(B * H * nb):
+        b, rem = divmod(r, H * nb)
+        h, i = divmod(rem, nb)
+        for e in range(rp[r], rp[r + 1]):
+            bits = fkeep[b, h, i, ci[e]]
+            fmask[e] = int(sum(1 << t for t in range(bt) if bits[t]))
+    res.update(frame_keep=fkeep, frame_mask=fmask, frame_diag=diag, frame_counts=counts)
+    return res
+
+
+def sparse_attention_frames(Q, K, V, geo: Geometry, row_ptr, col_idx, frame_mask,
+                            rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """sparse_attention restricted to the kept frames: for each real query
+    token of block i, one softmax over the real keys of the kept frames of the
+    kept blocks of row (b, h, i) (frame_mask aligned with col_idx, bit tau for
+    frame tau), scale 1/sqrt(d).  Outputs of rows not computed are NaN."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, N, H, d = Q.shape
+    nb = geo.nb
+    bt = geo.block[0]
+    members = block_members(geo)
+    fm = frame_members(geo)
+    O = np.full((B, N, H, d), np.nan)
+    row_ptr = np.asarray(row_ptr)
+    col_idx = np.asarray(col_idx)
+    frame_mask = np.asarray(frame_mask)
+    todo = range(B * H * nb) if rows is None else rows
+    for r in todo:
+        b, rem = divmod(int(r), H * nb)
+        h, i = divmod(rem, nb)
+        qtok = members[i][members[i] >= 0]
+        parts = []
+        for e in range(row_ptr[r], row_ptr[r + 1]):
+            j = int(col_idx[e])
+            for tau in range(bt):
+                if (int(frame_mask[e]) >> tau) & 1:
+                    parts.append(fm[j, tau][fm[j, tau] >= 0])
+        ktok = np.concatenate(parts)
+        logits = Q[b, qtok, h, :] @ K[b, ktok, h, :].T / math.sqrt(d)
+        logits -= logits.max(axis=1, keepdims=True)
+        w = np.exp(logits)
+        w /= w.sum(axis=1, keepdims=True)
+        O[b, qtok, h, :] = w @ V[b, ktok, h, :]
+    return O
+
+
+# --------------------------------------------------------------------------
 # Attention
 # --------------------------------------------------------------------------
 def sparse_attention(Q, K, V, geo: Geometry, row_ptr, col_idx,
