@@ -31,7 +31,8 @@ EXPORTS = ("abs_plan_init", "abs_route", "abs_attend_prepare", "abs_attend_run",
            "abs_attend", "abs_attend_grid", "abs_status_string", "abs_attend_split_ws_bytes",
            "abs_attend_prepare_split", "abs_attend_run_split", "abs_route_dynamic",
            "abs_slack_budget", "abs_attend_relayout", "abs_attend_schedule",
-           "abs_attend_default_sched", "abs_route_noalloc")
+           "abs_attend_default_sched", "abs_route_noalloc", "abs_route_frames",
+           "abs_attend_frames")
 # bytes of the static device scratch abs_route_noalloc works in (include/abs.h)
 ROUTE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -92,6 +93,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "abs_attend_schedule": [P, M, I32, V, SZ, V],
         "abs_slack_budget": [P, I32, V, F, ctypes.c_int64, V, V],
         "abs_route_noalloc": [P, V, V, F, I32, F, M, V],
+        "abs_route_frames": [P, V, V, F, I32, F, M, V, V, SZ, V],
+        "abs_attend_frames": [P, V, V, V, M, V, V, I32, V, SZ, V, V],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -208,6 +211,42 @@ def route_noalloc(plan: Plan, q, k, p: float, k_floor: int, slack: float = 0.0,
                                           _stream(stream))
     _check("abs_route_noalloc", st)
     return mask
+
+
+def route_frames(plan: Plan, q, k, p: float, k_floor: int, p_frame: float,
+                 mask: Optional[Mask] = None, frame_mask=None, ws=None, stream=None):
+    """Block routing, then Top-p over the frames of each row's kept blocks.
+    Returns (mask, frame_mask): frame_mask int32 aligned with mask.col_idx,
+    bit tau set when frame tau of that block is kept."""
+    torch = _check_qkv(plan, q, k)
+    mask = Mask(plan, q.device) if mask is None else mask
+    if frame_mask is None:
+        frame_mask = torch.empty(int(plan.col_capacity), dtype=torch.int32, device=q.device)
+    ws = workspace(plan.route_ws_bytes, q.device) if ws is None else ws
+    cm = mask.c()
+    st = load_library().abs_route_frames(ctypes.byref(plan), _ptr(q), _ptr(k), float(p),
+                                         int(k_floor), float(p_frame), ctypes.byref(cm),
+                                         _ptr(frame_mask), _ptr(ws), ws.numel(), _stream(stream))
+    _check("abs_route_frames", st)
+    return mask, frame_mask
+
+
+def attend_frames(plan: Plan, q, k, v, mask: Mask, frame_mask, sched: Optional[int] = None,
+                  o=None, ws=None, telemetry=None, stream=None):
+    """Block-sparse attention over the kept frames of the kept blocks; returns
+    o [B, N, H, d]."""
+    torch = _check_qkv(plan, q, k, v)
+    sched = default_sched(plan) if sched is None else sched
+    o = torch.empty_like(q) if o is None else o
+    ws = workspace(plan.attend_ws_bytes, q.device) if ws is None else ws
+    cm = mask.c()
+    tp = ctypes.c_void_p(0) if telemetry is None else _ptr(telemetry)
+    _check("abs_attend_frames",
+           load_library().abs_attend_frames(ctypes.byref(plan), _ptr(q), _ptr(k), _ptr(v),
+                                            ctypes.byref(cm), _ptr(frame_mask), _ptr(o),
+                                            int(sched), _ptr(ws), ws.numel(), tp,
+                                            _stream(stream)))
+    return o
 
 
 def route_dynamic(plan: Plan, q, k, p: float, k_floor: int, theta: float, budget,

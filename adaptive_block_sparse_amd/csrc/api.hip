@@ -37,7 +37,7 @@ Geo make_geo(const abs_plan* plan) {
   return g;
 }
 
-RouteWs route_ws_layout(const Geo& g, bool slack) {
+RouteWs route_ws_layout(const Geo& g, bool slack, bool frames) {
   RouteWs L;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
@@ -49,6 +49,9 @@ RouteWs route_ws_layout(const Geo& g, bool slack) {
   L.count = take((size_t)g.rows * sizeof(int));
   const size_t heads = (size_t)g.B * g.H;
   L.gsum = take(heads * route_groups_per_head(g.nb) * sizeof(int));
+  L.kf = take(frames ? heads * g.nb * g.bt * g.d * sizeof(float) : 0);
+  L.fbitmap = take(frames ? (size_t)g.rows * route_frame_words(g) * sizeof(uint32_t) : 0);
+  L.fcount = take(frames ? (size_t)g.rows * sizeof(int) : 0);
   L.hist = take(slack ? heads * 2048 * sizeof(uint32_t) : 0);
   L.sel = take(slack ? heads * 4 * sizeof(int) : 0);
   L.eqcnt = take(slack ? (size_t)g.rows * sizeof(int) : 0);
@@ -157,7 +160,7 @@ abs_status abs_plan_init(const abs_shape* shape, abs_plan* out) {
   if (hpp > (long long)s.batch * s.heads) hpp = (long long)s.batch * s.heads;
   p.heads_per_phase = (int32_t)hpp;
   Geo g = make_geo(&p);
-  p.route_ws_bytes = route_ws_layout(g, true).total;
+  p.route_ws_bytes = route_ws_layout(g, true, true).total;
   p.attend_ws_bytes = attend_ws_layout(g, s.dtype).total;
   *out = p;
   return ABS_OK;
@@ -193,6 +196,46 @@ abs_status abs_route_dynamic(const abs_plan* plan, const void* q, const void* k,
   hipError_t e = launch_route_dynamic(g, plan->s.dtype, q, k, p, kf, theta,
                                       (const long long*)budget, mask, (char*)ws, L,
                                       (hipStream_t)stream);
+  return e == hipSuccess ? ABS_OK : ABS_EHIP;
+}
+
+abs_status abs_route_frames(const abs_plan* plan, const void* q, const void* k, float p,
+                            int32_t k_floor, float p_frame, const abs_mask* mask,
+                            int32_t* frame_mask, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan_ok(plan) || !q || !k || !mask_ok(mask) || !frame_mask || !ws) return ABS_EINVAL;
+  if (!(p > 0.0f && p <= 1.0f) || !(p_frame > 0.0f && p_frame <= 1.0f)) return ABS_EINVAL;
+  if (k_floor < 1) return ABS_EINVAL;
+  Geo g = make_geo(plan);
+  if (g.bt > MAX_FRAMES || (long)g.nb * g.bt > MAX_FRAME_KEYS) return ABS_ENOTSUP;
+  RouteWs L = route_ws_layout(g, false, true);
+  if (ws_bytes < L.total) return ABS_ENOSPACE;
+  hipError_t e = launch_route_frames(g, plan->s.dtype, q, k, p, k_floor, p_frame, mask,
+                                     frame_mask, (char*)ws, L, (hipStream_t)stream);
+  return e == hipSuccess ? ABS_OK : ABS_EHIP;
+}
+
+abs_status abs_attend_frames(const abs_plan* plan, const void* q, const void* k, const void* v,
+                             const abs_mask* mask, const int32_t* frame_mask, void* o,
+                             int32_t sched, void* ws, size_t ws_bytes, int64_t* telemetry,
+                             void* stream) {
+  if (!plan_ok(plan) || !q || !k || !v || !o || !mask_ok(mask) || !frame_mask || !ws)
+    return ABS_EINVAL;
+  if (sched < ABS_SCHED_NNZ_SORTED || sched > ABS_SCHED_XCD_LOCAL) return ABS_EINVAL;
+  if (plan->s.dtype != ABS_BF16 || plan->block_tokens != 128) return ABS_ENOTSUP;
+  Geo g = make_geo(plan);
+  if (g.bt > MAX_FRAMES) return ABS_ENOTSUP;
+  AttendWs L = attend_ws_layout(g, plan->s.dtype);
+  if (ws_bytes < L.total) return ABS_ENOSPACE;
+  const int grid = attend_grid(g, plan->s.dtype, sched);
+  if (grid <= 0) return ABS_EHIP;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_attend_relayout(g, plan->s.dtype, k, v, (char*)ws, L, s);
+  if (e == hipSuccess)
+    e = launch_attend_schedule(g, plan->s.dtype, mask, sched, plan->heads_per_phase, (char*)ws,
+                               L, s, frame_mask);
+  if (e == hipSuccess)
+    e = launch_attend_run(g, plan->s.dtype, q, k, mask, o, sched, (char*)ws, L, telemetry, grid, s,
+                          true);
   return e == hipSuccess ? ABS_OK : ABS_EHIP;
 }
 

@@ -344,16 +344,25 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
 // position, and every kept block is written in ascending order from there.  The
 // list of item i starts at tlist[i * cap], cap = 2 nb, with tcount[i] entries.
 // ---------------------------------------------------------------------------
+//
+// With frame masks (fine-grained routing: frame_mask[e] bit tau = frame tau of
+// col_idx[e] kept), a row owns a block only if it keeps one of its frames, the
+// entry also holds the kept frames of the first block's row << 19 and of the
+// second's << 25 (at most 6 frames a block), and short also marks a block whose
+// kept frames (of either row) all sit in the first 64 slots.
+template <bool FR = false>
 __global__ __launch_bounds__(256) void tile_list_kernel(Geo g, const int* __restrict__ row_ptr,
                                                         const int* __restrict__ col_idx, int cap,
                                                         int* __restrict__ tlist,
                                                         int* __restrict__ tcount,
-                                                        int* __restrict__ icost) {
+                                                        int* __restrict__ icost,
+                                                        const int* __restrict__ frame_mask = nullptr) {
   constexpr int NT = 256, MAXW = MAX_NB / 32;
   static_assert(MAXW <= NT, "one bitmap word per thread");
   __shared__ uint32_t bA[MAXW], bB[MAXW], bS[MAXW];   // kept by A, by B; short blocks
   __shared__ int woff[MAXW];                           // list position of each word's first
   __shared__ int tmp[NT / 64 + 1];
+  __shared__ uint8_t fA[FR ? MAX_NB : 1], fB[FR ? MAX_NB : 1];   // frames kept by A, by B
   const int item = blockIdx.x;
   const int bhh = item / g.groups_per_head, gl = item % g.groups_per_head;
   int lead, partner;
@@ -369,19 +378,42 @@ __global__ __launch_bounds__(256) void tile_list_kernel(Geo g, const int* __rest
   const int W = (g.nb + 31) / 32;
   for (int w = threadIdx.x; w < W; w += NT) { bA[w] = 0u; bB[w] = 0u; bS[w] = 0u; }
   __syncthreads();
-  for (int j = threadIdx.x; j < g.nb; j += NT) {
-    const int e = block_extent(g, j);
-    if ((e & 255) * ((e >> 8) & 255) * ((e >> 16) & 255) <= 64)
-      atomicOr(&bS[j >> 5], 1u << (j & 31));
-  }
+  if constexpr (FR)
+    for (int j = threadIdx.x; j < g.nb; j += NT) { fA[j] = 0; fB[j] = 0; }
+  if constexpr (!FR)
+    for (int j = threadIdx.x; j < g.nb; j += NT) {
+      const int e = block_extent(g, j);
+      if ((e & 255) * ((e >> 8) & 255) * ((e >> 16) & 255) <= 64)
+        atomicOr(&bS[j >> 5], 1u << (j & 31));
+    }
   for (int i = threadIdx.x; i < nA; i += NT) {
     const int v = col_idx[pA + i];
+    if (FR) {
+      const int fm = frame_mask[pA + i];
+      if (fm == 0) continue;
+      fA[v] = (uint8_t)fm;
+    }
     atomicOr(&bA[v >> 5], 1u << (v & 31));
   }
   for (int i = threadIdx.x; i < nB; i += NT) {
     const int v = col_idx[pB + i];
+    if (FR) {
+      const int fm = frame_mask[pB + i];
+      if (fm == 0) continue;
+      fB[v] = (uint8_t)fm;
+    }
     atomicOr(&bB[v >> 5], 1u << (v & 31));
   }
+  __syncthreads();
+  if constexpr (FR)
+    for (int j = threadIdx.x; j < g.nb; j += NT) {
+      // short: the real tokens of every kept frame lie in the first 64 slots
+      const int e = block_extent(g, j);
+      const int fs = ((e >> 8) & 255) * ((e >> 16) & 255);   // tokens per frame
+      const int u = fA[j] | fB[j];
+      const int top = u ? 31 - __clz(u) : 0;                 // highest kept frame
+      if (u && (top + 1) * fs <= 64) atomicOr(&bS[j >> 5], 1u << (j & 31));
+    }
   __syncthreads();
   {
     const int w = threadIdx.x;
@@ -401,7 +433,9 @@ __global__ __launch_bounds__(256) void tile_list_kernel(Geo g, const int* __rest
     if (!(((a | b) >> bit) & 1u)) continue;
     const int pos = woff[wj] + __popc((a | b) & ((1u << bit) - 1u));
     const int owners = (int)((a >> bit) & 1u) | ((int)((b >> bit) & 1u) << 1);
-    out[pos] = j | ((int)((bS[wj] >> bit) & 1u) << 16) | (owners << 17);
+    int ent = j | ((int)((bS[wj] >> bit) & 1u) << 16) | (owners << 17);
+    if constexpr (FR) ent |= ((int)fA[j] << 19) | ((int)fB[j] << 25);
+    out[pos] = ent;
   }
   if (threadIdx.x == 0) icost[item] = nA + nB;
 }
@@ -596,9 +630,10 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
                : "memory", "m0");
 }
 
-template <int D, int BT, bool PERSIST, bool SPLIT = false>
+template <int D, int BT, bool PERSIST, bool SPLIT = false, bool FRAMES = false>
 __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs a) {
   static_assert(PERSIST || !SPLIT, "split units come from the persistent queue");
+  static_assert(!FRAMES || (BT == 128 && !SPLIT), "frame masks: 128-token blocks, whole items");
   using C = AttnCfg<D, BT>;
   __shared__ __attribute__((aligned(1024))) char sK[2][C::TILE];
   __shared__ __attribute__((aligned(1024))) char sV[2][C::TILE];
@@ -622,8 +657,24 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
     const int e = block_extent(g, j);
     return (e & 255) * ((e >> 8) & 255) * ((e >> 16) & 255);   // real tokens
   };
+  // fine-grained routing: beside the real count (bits 0-7), for each 32-key
+  // subtile t of the tile the first and last frame its real keys belong to
+  // (3 bits each, at bit 8 + 6t)
+  auto block_info_frames = [&](int j) {
+    const int e = block_extent(g, j);
+    const int fs = ((e >> 8) & 255) * ((e >> 16) & 255);   // real tokens per frame
+    const int nreal = (e & 255) * fs;
+    int info = nreal;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (32 * t < nreal) {
+        const int fa = (32 * t) / fs, fb = (min(32 * t + 32, nreal) - 1) / fs;
+        info |= (fa | (fb << 3)) << (8 + 6 * t);
+      }
+    return info;
+  };
   if constexpr (BINFO)
-    for (int j = tid; j < g.nb; j += C::NT) s_binfo[j] = block_info(j);
+    for (int j = tid; j < g.nb; j += C::NT) s_binfo[j] = FRAMES ? block_info_frames(j) : block_info(j);
   __syncthreads();
 
   const uint32_t sK_base = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)&sK[0][0];
@@ -737,6 +788,7 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
     int e2 = nt > 2 ? ld_scalar(tl, 2) : -1;
     if (e0 >= 0) issue(e0, 0);
 
+
     // this lane's query slot (packed slot order, see packed_slot_offset)
     const int tq = iq / (g.nbh * g.nbw), hq = (iq / g.nbw) % g.nbh, wqb = iq % g.nbw;
     const int n0q = ((tq * g.bt) * g.Hg + hq * g.bh) * g.W + wqb * g.bw;
@@ -775,18 +827,37 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
     for (int t = 0; t < nt; ++t) {
       const int j = e0 & 0xffff;
       const bool mine = ((e0 >> (17 + half)) & 1) != 0;
+      // fine-grained routing: this wave's row's kept frames of block j
+      const int fmw = FRAMES ? (e0 >> (19 + 6 * half)) & 63 : 0;
       const int en = e1;
       if constexpr (SPLIT) tiles += ((e0 >> 17) & 1) + ((e0 >> 18) & 1);   // owned tiles
       e0 = e1;
       e1 = e2;
       e2 = __builtin_amdgcn_readfirstlane(t + 3 < nt ? ld_scalar(tl, t + 3) : -1);
 
+
       wait_vmcnt<0>();      // this thread's copies of block j have landed
       wg_barrier();         // ... everyone's; and block j-1's buffer is free
       if (en >= 0) issue(en, buf ^ 1);
 
       if (mine && wave_has_q) {
-        const int nreal = __builtin_amdgcn_readfirstlane(BINFO ? s_binfo[j] : block_info(j));
+        const int info = __builtin_amdgcn_readfirstlane(BINFO ? s_binfo[j] : block_info(j));
+        const int nreal = FRAMES ? (info & 255) : info;
+        // fine-grained routing: fpart when this wave's row keeps only some of
+        // the block's frames (the last real key's frame is the last frame); else
+        // the tile runs as without frame masks
+        bool fpart = false;
+        if constexpr (FRAMES) {
+          const int last = (info >> (11 + 6 * ((nreal - 1) >> 5))) & 7;
+          fpart = fmw != (2 << last) - 1;
+        }
+        // kept frames among the real keys of subtiles ta..tb (ta <= tb, both
+        // holding real keys): 2 all, 1 some, 0 none
+        auto frames_in = [&](int ta, int tb) {
+          const int fa = (info >> (8 + 6 * ta)) & 7, fb = (info >> (11 + 6 * tb)) & 7;
+          const int m = ((2 << fb) - 1) & ~((1 << fa) - 1);
+          return (fmw & m) == m ? 2 : ((fmw & m) != 0 ? 1 : 0);
+        };
         const char* kb = sK[buf] + kread;
         const char* vb = sV[buf] + vread;
 #pragma unroll
@@ -794,10 +865,17 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
           // a chunk whose first slot lies beyond the block's real tokens holds
           // only padding keys: nothing to add
           if (hc * C::CHS * 32 >= nreal) continue;
-          // only when the chunk's second subtile holds real keys are its score
-          // and PV products run (else its scores are the padding bias alone and
-          // its probabilities zero)
-          const bool two = C::CHS == 1 || (hc * C::CHS + 1) * 32 < nreal;
+          // fine-grained routing: a chunk none of whose real keys lies in a kept
+          // frame of this wave's row adds nothing either
+          if (FRAMES && fpart &&
+              frames_in(hc * C::CHS, (hc * C::CHS + 1) * 32 < nreal ? hc * C::CHS + C::CHS - 1
+                                                                     : hc * C::CHS) == 0)
+            continue;
+          // only when the chunk's second subtile holds real keys (of kept
+          // frames) are its score and PV products run (else its scores are the
+          // bias alone and its probabilities zero)
+          bool two = C::CHS == 1 || (hc * C::CHS + 1) * 32 < nreal;
+          if (FRAMES && fpart && two && C::CHS == 2) two = frames_in(hc * 2 + 1, hc * 2 + 1) != 0;
           // Waves w and w + NW1 share a SIMD and would otherwise run the same
           // phases in step.  Their priorities alternate: chunk by chunk, one
           // half leads the score products and the other the softmax and PV
@@ -819,9 +897,20 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
 #pragma unroll
           for (int t2 = 0; t2 < C::CHS; ++t2) {
             const int t = hc * C::CHS + t2;
-            // padding keys: add -1e30 through one extra k-step (bias column x ones row)
-            auto add_bias = [&](const f32x16_t& acc) {
-              const bool ok = 32 * t + l32 < nreal;
+            // padding keys: add -1e30 through one extra k-step (bias column x ones row).
+            // fmode (fine-grained routing): 1 also masks the keys of frames the
+            // row does not keep, 2 masks every key of the subtile
+            auto add_bias = [&](const f32x16_t& acc, int fmode) {
+              bool ok = 32 * t + l32 < nreal;
+              if (FRAMES && fmode == 2) ok = false;
+              if (FRAMES && fmode == 1) {
+                const int e = block_extent(g, j);
+                const float fs = (float)(((e >> 8) & 255) * ((e >> 16) & 255));
+                // frame of the lane's key slot: floor((s + 1/2) / fs) is exact in
+                // float32 for slots and frame sizes below 256
+                const int f = (int)(((float)(32 * t + l32) + 0.5f) / fs);
+                ok = ok && ((fmw >> f) & 1);
+              }
               bf16x8_t bias, ones;
 #pragma unroll
               for (int e = 0; e < 8; ++e) { bias[e] = (__bf16)0.0f; ones[e] = (__bf16)0.0f; }
@@ -843,10 +932,14 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
                 __builtin_amdgcn_sched_barrier(0);
               }
               // only the subtile that holds the block's last real key also
-              // holds padding keys
-              if (32 * (t + 1) > nreal) s[t2] = add_bias(s[t2]);
+              // holds padding keys (and, with frame masks, a subtile that
+              // holds keys of a frame its row does not keep)
+              const bool fsub = FRAMES && fpart && frames_in(t, t) != 2;
+              if (32 * (t + 1) > nreal || fsub) s[t2] = add_bias(s[t2], fsub ? 1 : 0);
             } else {
-              s[t2] = add_bias(zero);   // padding keys only: the scores are the bias alone
+              // padding keys only (or, with frame masks, keys of frames the row
+              // does not keep): the scores are the bias alone
+              s[t2] = add_bias(zero, 2);
             }
           }
 
@@ -1172,11 +1265,15 @@ hipError_t launch_attend_prepare(const Geo& g, int dtype, const void* k, const v
 
 hipError_t launch_attend_schedule(const Geo& g, int dtype, const abs_mask* mask, int sched,
                                   int heads_per_phase, char* ws, const AttendWs& L,
-                                  hipStream_t s) {
-  if (dtype == ABS_BF16)
-    hipLaunchKernelGGL(tile_list_kernel, dim3(g.groups), dim3(256), 0, s, g, mask->row_ptr,
+                                  hipStream_t s, const int* frame_mask) {
+  if (dtype == ABS_BF16 && frame_mask)
+    hipLaunchKernelGGL(tile_list_kernel<true>, dim3(g.groups), dim3(256), 0, s, g, mask->row_ptr,
                        mask->col_idx, tlist_cap(g), (int*)(ws + L.tlist), (int*)(ws + L.tcount),
-                       (int*)(ws + L.icost));
+                       (int*)(ws + L.icost), frame_mask);
+  else if (dtype == ABS_BF16)
+    hipLaunchKernelGGL(tile_list_kernel<false>, dim3(g.groups), dim3(256), 0, s, g, mask->row_ptr,
+                       mask->col_idx, tlist_cap(g), (int*)(ws + L.tlist), (int*)(ws + L.tcount),
+                       (int*)(ws + L.icost), (const int*)nullptr);
   // head-phased work items: one workgroup per phase
   const int grid = sched == ABS_SCHED_HEAD_PHASED
                        ? (g.B * g.H + heads_per_phase - 1) / heads_per_phase : 1;
@@ -1192,9 +1289,9 @@ hipError_t launch_attend_prepare_split(const Geo& g, const void* k, const void* 
                                        int split_tiles, int max_parts, char* ws,
                                        const AttendWs& L, hipStream_t s) {
   launch_relayout_bf16(g, k, v, ws, L, s);
-  hipLaunchKernelGGL(tile_list_kernel, dim3(g.groups), dim3(256), 0, s, g, mask->row_ptr,
+  hipLaunchKernelGGL(tile_list_kernel<false>, dim3(g.groups), dim3(256), 0, s, g, mask->row_ptr,
                      mask->col_idx, tlist_cap(g), (int*)(ws + L.tlist), (int*)(ws + L.tcount),
-                       (int*)(ws + L.icost));
+                     (int*)(ws + L.icost), (const int*)nullptr);
   hipLaunchKernelGGL(split_units_kernel, dim3(1), dim3(1024), 0, s, g, (const int*)(ws + L.tcount),
                      split_tiles, max_parts, (int4*)(ws + L.units), (int4*)(ws + L.stab),
                      (int*)(ws + L.counter));
@@ -1244,12 +1341,14 @@ int attend_grid(const Geo& g, int dtype, int sched) {
   return persistent_grid<64, 32>();
 }
 
-template <int D, int BT>
+template <int D, int BT, bool FR = false>
 static void launch_bf16(const AttnArgs& a, bool persist, int grid, hipStream_t s) {
   if (persist)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, BT, true>), dim3(grid), dim3(4 * BT), 0, s, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, BT, true, false, FR>), dim3(grid), dim3(4 * BT), 0, s,
+                       a);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, BT, false>), dim3(grid), dim3(4 * BT), 0, s, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, BT, false, false, FR>), dim3(grid), dim3(4 * BT), 0,
+                       s, a);
 }
 
 template <int D, int BT>
@@ -1259,7 +1358,8 @@ static void launch_bf16_split(const AttnArgs& a, int grid, hipStream_t s) {
 
 hipError_t launch_attend_run(const Geo& g, int dtype, const void* q, const void* k,
                              const abs_mask* mask, void* o, int sched, char* ws,
-                             const AttendWs& L, int64_t* telemetry, int grid, hipStream_t s) {
+                             const AttendWs& L, int64_t* telemetry, int grid, hipStream_t s,
+                             bool frames) {
   const int* sch = (const int*)(ws + L.sched);
   const bool head_major = sched == ABS_SCHED_HEAD_MAJOR;
   if (dtype == ABS_BF16) {
@@ -1282,7 +1382,10 @@ hipError_t launch_attend_run(const Geo& g, int dtype, const void* q, const void*
     a.tcount = (const int*)(ws + L.tcount);
     a.tlist_cap = tlist_cap(g);
     if (persist) hipLaunchKernelGGL(reset_counter_kernel, dim3(1), dim3(64), 0, s, a.counter);
-    if (g.d == 128) {
+    if (frames) {
+      if (g.d == 128) launch_bf16<128, 128, true>(a, persist, grid, s);
+      else launch_bf16<64, 128, true>(a, persist, grid, s);
+    } else if (g.d == 128) {
       if (g.Bt == 128) launch_bf16<128, 128>(a, persist, grid, s);
       else if (g.Bt == 64) launch_bf16<128, 64>(a, persist, grid, s);
       else launch_bf16<128, 32>(a, persist, grid, s);

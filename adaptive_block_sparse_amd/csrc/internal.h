@@ -96,14 +96,15 @@ hipError_t launch_attend_relayout(const Geo& g, int dtype, const void* k, const 
                                   char* ws, const AttendWs& L, hipStream_t s);
 hipError_t launch_attend_schedule(const Geo& g, int dtype, const abs_mask* mask, int sched,
                                   int heads_per_phase, char* ws, const AttendWs& L,
-                                  hipStream_t s);
+                                  hipStream_t s, const int* frame_mask = nullptr);
 hipError_t launch_attend_prepare(const Geo& g, int dtype, const void* k, const void* v,
                                  const abs_mask* mask,
                                  int sched, int heads_per_phase, char* ws, const AttendWs& L,
                                  hipStream_t s);
 hipError_t launch_attend_run(const Geo& g, int dtype, const void* q, const void* k,
                              const abs_mask* mask, void* o, int sched, char* ws,
-                             const AttendWs& L, int64_t* telemetry, int grid, hipStream_t s);
+                             const AttendWs& L, int64_t* telemetry, int grid, hipStream_t s,
+                             bool frames = false);
 // Split-and-merge variants (bf16): heavy work items cut into parts along their
 // union tile lists, partial results merged by log-sum-exp weights.
 hipError_t launch_attend_prepare_split(const Geo& g, const void* k, const void* v,
@@ -125,6 +126,8 @@ constexpr int NUNITS = 48;       // counter[NUNITS]: work units of the split-and
 constexpr int NSPLIT = 49;       // counter[NSPLIT]: items cut into two or more parts
 constexpr int MAX_SPLIT_PARTS = 1 << 24;   // bound on max_parts (slot indices stay int32)
 constexpr int MAX_NB = 4096;     // key blocks per head supported by the plan
+constexpr int MAX_FRAMES = 6;    // fine-grained routing: frames per block (block[0])
+constexpr int MAX_FRAME_KEYS = 1024;   // fine-grained routing: frames per head (nb * bt)
 inline int tlist_cap(const Geo& g) { return 2 * g.nb; }   // union entries per item
 // floats of one partial-result slot: O^T for the item's two query blocks, then
 // the reference maximum (exp2 domain) and the sum of each query

@@ -94,6 +94,72 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo g, const T* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// Frame means of K (fine-grained routing): for every 3D block and temporal
+// offset tau < bt, the mean of K over the block's real tokens at that offset
+// (bh x bw tokens, fewer in a block cut by the grid edge); 0 for a frame with
+// no real token (a block cut along t).  Grid and thread layout as pool_kernel;
+// the frames are summed one after the other.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void frame_pool_kernel(Geo g, const T* __restrict__ k,
+                                                         float* __restrict__ kf, int hg) {
+  constexpr int E = Chunk<T>::E;
+  constexpr int C = D / E;
+  constexpr int BATCH = 8;
+  __shared__ float red[256 * E];
+  const int run = hg * C, tpp = 256 / run;
+  const int ngrp = g.H / hg;
+  const int b = blockIdx.x / ngrp, h0 = (blockIdx.x % ngrp) * hg;
+  const int blk = blockIdx.y;
+  const int tb = blk / (g.nbh * g.nbw), hb = (blk / g.nbw) % g.nbh, wb = blk % g.nbw;
+  const int Tl = min(g.bt, g.T - tb * g.bt), Hl = min(g.bh, g.Hg - hb * g.bh),
+            Wl = min(g.bw, g.W - wb * g.bw);
+  const float inv = 1.0f / (float)(Hl * Wl);
+  const int c = threadIdx.x % run, sub = threadIdx.x / run;
+  const int plane = g.bh * g.bw;   // slots of one frame
+  const long tok = (long)g.H * D;
+  const long base = (long)b * g.N * tok + (long)h0 * D + c * E;
+  const int outs = run * E;
+  for (int tau = 0; tau < g.bt; ++tau) {
+    float ak[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) ak[e] = 0.f;
+    if (tau < Tl) {
+      for (int s0 = sub; s0 < plane; s0 += BATCH * tpp) {
+        uint4 rk[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          const int s = s0 + u * tpp;
+          rk[u] = make_uint4(0u, 0u, 0u, 0u);
+          const int sh = s / g.bw, sw = s % g.bw;
+          if (s < plane && sh < Hl && sw < Wl) {
+            const long n = ((long)(tb * g.bt + tau) * g.Hg + hb * g.bh + sh) * g.W + wb * g.bw + sw;
+            rk[u] = *reinterpret_cast<const uint4*>(k + base + n * tok);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          float vk[E];
+          Chunk<T>::unpack(rk[u], vk);
+#pragma unroll
+          for (int e = 0; e < E; ++e) ak[e] += vk[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) red[threadIdx.x * E + e] = ak[e];
+    __syncthreads();
+    for (int o = threadIdx.x; o < outs; o += 256) {
+      float sum = 0.f;
+      for (int s = 0; s < tpp; ++s) sum += red[s * outs + o];
+      kf[((((long)b * g.H + h0 + o / D) * g.nb + blk) * g.bt + tau) * D + o % D] =
+          tau < Tl ? sum * inv : 0.f;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Wave-wide sum and maximum through DPP row operations (quad swaps, half-row
 // and row mirrors) and the four row results read out in a fixed order, so
 // every lane receives the same value.
@@ -192,11 +258,19 @@ __device__ __forceinline__ float row16_max(float x) {
 // block is added last.  Output: the rows' bitmaps and counts, the group's
 // total count (for the CSR offsets) and, for slack fills, P.
 // ---------------------------------------------------------------------------
-template <int D, int NC>
+//
+// FR: the same selection one level down (fine-grained Top-p inside the kept
+// blocks): the keys are the frames f = j*bt + tau of the blocks (kp then holds
+// the frame means of K, nk = nb*bt per head), and only the real frames of the
+// blocks the row keeps in `cand` (the block-level bitmaps) are candidates.  The
+// floor counts frames, every frame of the own block is kept, and the output is
+// the row's frame bitmap.
+template <int D, int NC, bool FR = false>
 __global__ __launch_bounds__(256) void route_select_kernel(
     Geo g, const float* __restrict__ qp, const float* __restrict__ kp,
     uint32_t* __restrict__ bitmap, int* __restrict__ count, int* __restrict__ gsum,
-    float* __restrict__ prob, float p, int k_floor, float scale) {
+    float* __restrict__ prob, float p, int k_floor, float scale,
+    const uint32_t* __restrict__ cand, int nk, int words_out) {
   constexpr int KS = D + 4;          // padded LDS row of one key block's mean
   constexpr int TS = 64 * NC + 16;   // padded LDS row of one row's scores
   constexpr int E = 4 * NC;          // elements per lane in the 16-lane layout
@@ -208,9 +282,9 @@ __global__ __launch_bounds__(256) void route_select_kernel(
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int nb = g.nb;
-  const int nch = (nb + 63) >> 6;    // key chunks present (<= NC)
+  const int nch = (nk + 63) >> 6;    // key chunks present (<= NC)
   const int ig = blockIdx.x * 16;    // first row of the group
-  const float* K = kp + (long)bh * nb * D;
+  const float* K = kp + (long)bh * nk * D;
   // Scores on the fp32 matrix cores (v_mfma_f32_16x16x4_f32): the group's 16
   // rows against 16 keys per wave and chunk.  Lane l supplies A[l % 16][l / 16]
   // and B[l / 16][l % 16] and receives D[4 (l / 16) + r][l % 16] in register r.
@@ -237,7 +311,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(
       const int kb = f / (D / 4), d4 = f % (D / 4);
       const int j = c * 64 + kb;
       nxt[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (j < nb) nxt[u] = *reinterpret_cast<const float4*>(K + (long)j * D + d4 * 4);
+      if (j < nk) nxt[u] = *reinterpret_cast<const float4*>(K + (long)j * D + d4 * 4);
     }
   };
   load_chunk(0);
@@ -272,7 +346,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     const int j = c * 64 + 16 * wv + a16;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      lds[(4 * kq + r) * TS + j] = c < nch && j < nb ? acc[c][r] * scale : -INFINITY;
+      lds[(4 * kq + r) * TS + j] = c < nch && j < nk ? acc[c][r] * scale : -INFINITY;
   }
   __syncthreads();
   const float* T = lds + wv * 4 * TS;
@@ -282,10 +356,29 @@ __global__ __launch_bounds__(256) void route_select_kernel(
   const bool live = i < nb;
   const int row = bh * nb + i;
   float x[E];
+  bool valid[E];
+  int nc = nb;                       // candidates of the row
 #pragma unroll
-  for (int e = 0; e < E; ++e) x[e] = T[rr * TS + 16 * e + l16];
+  for (int e = 0; e < E; ++e) {
+    const int f = 16 * e + l16;
+    valid[e] = f < nk;
+    if constexpr (FR) {
+      // a frame of a block the row keeps, and a frame with real tokens
+      const int j = f / g.bt, tau = f - j * g.bt;
+      const int tl = min(g.bt, g.T - (j / (g.nbh * g.nbw)) * g.bt);
+      valid[e] = valid[e] && live && tau < tl &&
+                 ((cand[(long)row * g.words + (j >> 5)] >> (j & 31)) & 1u);
+    }
+    x[e] = valid[e] ? T[rr * TS + f] : -INFINITY;
+  }
+  if constexpr (FR) {
+    int n = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) n += valid[e] ? 1 : 0;
+    nc = row16_sum_int(n);
+  }
 
-  // softmax over the row's nb blocks; keys = bit patterns of P, -1 past nb
+  // softmax over the row's candidates; keys = bit patterns of P, -1 elsewhere
   float mx = -INFINITY;
 #pragma unroll
   for (int e = 0; e < E; ++e) mx = fmaxf(mx, x[e]);
@@ -304,8 +397,8 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     const int j = 16 * e + l16;
     const float pj = x[e] * rz;
     if (prob && live && j < nb) prob[(long)row * nb + j] = pj;
-    key[e] = j < nb ? __float_as_int(pj) : -1;
-    part += j < nb ? pj : 0.f;
+    key[e] = valid[e] ? __float_as_int(pj) : -1;
+    part += valid[e] ? pj : 0.f;
   }
   const float total = row16_sum(part);
 
@@ -320,7 +413,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     kmax = max(kmax, key[e]);
   }
   int lo = row16_min_int(kmin), hi = row16_max_int(kmax) + 1;
-  int clo = nb, chi = 0;
+  int clo = nc, chi = 0;
   float shi = 0.f;
   bool active = clo - chi > 1 && hi - lo > 1;
   for (int step = 0; step < 31; ++step) {
@@ -359,8 +452,8 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     need = t < 1.f ? 1 : (t < (float)ct ? (int)t : ct);
   }
   const int m = cg + need;
-  const int m2 = min(nb, max(m, k_floor));
-  const bool all = p >= 1.0f || !(total >= p) || m2 >= nb;
+  const int m2 = min(nc, max(m, k_floor));
+  const bool all = p >= 1.0f || !(total >= p) || m2 >= nc;
   const bool floor_row = !all && m2 > m;
   int thr = all ? -1 : lo;           // keep key > thr, and the first ktie keys == thr
   int ktie = all ? 0 : need;
@@ -400,11 +493,13 @@ __global__ __launch_bounds__(256) void route_select_kernel(
     const uint32_t eg = (uint32_t)(__ballot(eq) >> sh) & 0xffffu;
     const int rank = tie_seen + __popc(eg & below);
     tie_seen += __popc(eg);
-    const bool keep = j < nb && (key[e] > thr || (eq && rank < ktie) || j == i);
+    const bool own = FR ? j / g.bt == i : j == i;
+    const bool keep = valid[e] && (key[e] > thr || (eq && rank < ktie) || own);
     const uint32_t kg = (uint32_t)(__ballot(keep) >> sh) & 0xffffu;
     kept += __popc(kg);
     if (e & 1) {
-      if (live && l16 == 0 && (e >> 1) < g.words) bitmap[(long)row * g.words + (e >> 1)] = half | (kg << 16);
+      if (live && l16 == 0 && (e >> 1) < words_out)
+        bitmap[(long)row * words_out + (e >> 1)] = half | (kg << 16);
     } else {
       half = kg;
     }
@@ -415,7 +510,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(
                    __builtin_amdgcn_readlane(mine, 32) + __builtin_amdgcn_readlane(mine, 48);
   if (lane == 0) wsum[wv] = wtot;
   __syncthreads();
-  if (threadIdx.x == 0)
+  if (threadIdx.x == 0 && gsum)
     gsum[bh * gridDim.x + blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
 }
 
@@ -890,12 +985,16 @@ __global__ __launch_bounds__(256) void route_gsum_kernel(Geo g, const int* __res
 // group of a head also writes the head's total, the last group the end of
 // row_ptr.
 // ---------------------------------------------------------------------------
+// With frame bitmaps (fine-grained routing, fwords words a row) every entry
+// also gets its kept frames: frame_mask[e] bit tau = frame tau of that block.
 __global__ __launch_bounds__(256) void route_csr_kernel(Geo g, const uint32_t* __restrict__ bitmap,
                                                         const int* __restrict__ count,
                                                         const int* __restrict__ gsum, int rpg,
                                                         int* __restrict__ row_ptr,
                                                         int* __restrict__ col_idx,
-                                                        int* __restrict__ head_nnz) {
+                                                        int* __restrict__ head_nnz,
+                                                        const uint32_t* __restrict__ fbitmap,
+                                                        int fwords, int* __restrict__ frame_mask) {
   __shared__ int tmp[8];
   __shared__ int roff[17];
   const int bh = blockIdx.y, x = blockIdx.x, gph = gridDim.x;
@@ -927,13 +1026,23 @@ __global__ __launch_bounds__(256) void route_csr_kernel(Geo g, const uint32_t* _
     const int row = bh * g.nb + i0 + r;
     const int start = base + roff[r];
     if (lane == 0) row_ptr[row] = start;
-    int* out = col_idx + start;
+    int pos = start;
     for (int c0 = 0; c0 < g.nb; c0 += 64) {
       const int j = c0 + lane;
       const bool bit = j < g.nb && ((bitmap[(long)row * g.words + (j >> 5)] >> (j & 31)) & 1u);
       const unsigned long long m = __ballot(bit);
-      if (bit) out[__popcll(m & ((1ull << lane) - 1ull))] = j;
-      out += __popcll(m);
+      if (bit) {
+        const int at = pos + __popcll(m & ((1ull << lane) - 1ull));
+        col_idx[at] = j;
+        if (frame_mask) {
+          const uint32_t* fb = fbitmap + (long)row * fwords;
+          const int f0 = j * g.bt, w0 = f0 >> 5, sh = f0 & 31;
+          uint32_t v = fb[w0] >> sh;
+          if (sh + g.bt > 32) v |= fb[w0 + 1] << (32 - sh);
+          frame_mask[at] = (int)(v & ((1u << g.bt) - 1u));
+        }
+      }
+      pos += __popcll(m);
     }
   }
 }
@@ -972,7 +1081,7 @@ static void launch_select16(const Geo& g, dim3 grid, const float* qp, const floa
                             uint32_t* bm, int* cnt, int* gsum, float* prob, float p, int kf,
                             float scale, hipStream_t s) {
   hipLaunchKernelGGL((route_select_kernel<D, NC>), grid, dim3(256), 0, s, g, qp, kp, bm, cnt, gsum,
-                     prob, p, kf, scale);
+                     prob, p, kf, scale, (const uint32_t*)nullptr, g.nb, g.words);
 }
 
 template <int D>
@@ -1012,7 +1121,7 @@ static void launch_route_front(const Geo& g, int dtype, const void* q, const voi
 }
 
 static void launch_route_csr(const Geo& g, char* ws, const RouteWs& L, bool recount,
-                             const abs_mask* mask, hipStream_t s) {
+                             const abs_mask* mask, hipStream_t s, int* frame_mask = nullptr) {
   const int rpg = route_group_rows(g.nb), gph = route_groups_per_head(g.nb);
   int* cnt = (int*)(ws + L.count);
   int* gsum = (int*)(ws + L.gsum);
@@ -1023,7 +1132,8 @@ static void launch_route_csr(const Geo& g, char* ws, const RouteWs& L, bool reco
   }
   hipLaunchKernelGGL(route_csr_kernel, dim3(gph, g.B * g.H), dim3(256), 0, s, g,
                      (const uint32_t*)(ws + L.bitmap), cnt, gsum, rpg, mask->row_ptr,
-                     mask->col_idx, mask->head_nnz);
+                     mask->col_idx, mask->head_nnz, (const uint32_t*)(ws + L.fbitmap),
+                     route_frame_words(g), frame_mask);
 }
 
 hipError_t launch_route(const Geo& g, int dtype, const void* q, const void* k, float p,
@@ -1085,6 +1195,71 @@ hipError_t launch_route_dynamic(const Geo& g, int dtype, const void* q, const vo
   hipLaunchKernelGGL(slack_mark_kernel, dim3(wg4), dim3(256), 0, s, g, prob, bm, cnt, sel, eqoff,
                      g.rows, theta);
   launch_route_csr(g, ws, L, true, mask, s);
+  return hipGetLastError();
+}
+
+template <int D, int NC>
+static void launch_select_frames_nc(const Geo& g, dim3 grid, const float* qp, const float* kf,
+                                    const uint32_t* cand, uint32_t* fbm, int* fcnt, float p,
+                                    int k_floor, float scale, hipStream_t s) {
+  hipLaunchKernelGGL((route_select_kernel<D, NC, true>), grid, dim3(256), 0, s, g, qp, kf, fbm,
+                     fcnt, (int*)nullptr, (float*)nullptr, p, k_floor, scale, cand, g.nb * g.bt,
+                     route_frame_words(g));
+}
+
+template <int D>
+static void launch_select_frames(const Geo& g, dim3 grid, const float* qp, const float* kf,
+                                 const uint32_t* cand, uint32_t* fbm, int* fcnt, float p,
+                                 int k_floor, float scale, hipStream_t s) {
+  const int nch = (g.nb * g.bt + 63) / 64;
+#define ABS_SELF(NC_)                                                                     \
+  if (nch <= NC_) {                                                                       \
+    launch_select_frames_nc<D, NC_>(g, grid, qp, kf, cand, fbm, fcnt, p, k_floor, scale, s); \
+    return;                                                                               \
+  }
+  ABS_SELF(2) ABS_SELF(4) ABS_SELF(6) ABS_SELF(8) ABS_SELF(10) ABS_SELF(12) ABS_SELF(16)
+#undef ABS_SELF
+}
+
+hipError_t launch_route_frames(const Geo& g, int dtype, const void* q, const void* k, float p,
+                               int k_floor, float p_frame, const abs_mask* mask, int* frame_mask,
+                               char* ws, const RouteWs& L, hipStream_t s) {
+  launch_route_front(g, dtype, q, k, p, k_floor, ws, L, nullptr, s);
+  // frame means of K
+  float* kf = (float*)(ws + L.kf);
+  {
+    const int cph = g.d * (dtype == ABS_BF16 ? 2 : 4) / 16;
+    int hg = 8;
+    while (hg > 1 && (g.H % hg != 0 || hg * cph > 256 || (long)g.B * (g.H / hg) * g.nb < 4096))
+      hg /= 2;
+    dim3 grid(g.B * (g.H / hg), g.nb);
+    if (dtype == ABS_BF16) {
+      if (g.d == 128)
+        hipLaunchKernelGGL((frame_pool_kernel<bf16_t, 128>), grid, dim3(256), 0, s, g,
+                           (const bf16_t*)k, kf, hg);
+      else
+        hipLaunchKernelGGL((frame_pool_kernel<bf16_t, 64>), grid, dim3(256), 0, s, g,
+                           (const bf16_t*)k, kf, hg);
+    } else {
+      if (g.d == 128)
+        hipLaunchKernelGGL((frame_pool_kernel<float, 128>), grid, dim3(256), 0, s, g,
+                           (const float*)k, kf, hg);
+      else
+        hipLaunchKernelGGL((frame_pool_kernel<float, 64>), grid, dim3(256), 0, s, g,
+                           (const float*)k, kf, hg);
+    }
+  }
+  const dim3 grid(route_groups_per_head(g.nb), g.B * g.H);
+  const float scale = (float)(1.0 / sqrt((double)g.d));
+  const float* qp = (const float*)(ws + L.qp);
+  const uint32_t* cand = (const uint32_t*)(ws + L.bitmap);
+  uint32_t* fbm = (uint32_t*)(ws + L.fbitmap);
+  int* fcnt = (int*)(ws + L.fcount);
+  if (g.d == 128)
+    launch_select_frames<128>(g, grid, qp, kf, cand, fbm, fcnt, p_frame, k_floor, scale, s);
+  else
+    launch_select_frames<64>(g, grid, qp, kf, cand, fbm, fcnt, p_frame, k_floor, scale, s);
+  launch_route_csr(g, ws, L, false, mask, s, frame_mask);
   return hipGetLastError();
 }
 

@@ -237,6 +237,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--p", type=float, default=None)
+    ap.add_argument("--frames", type=float, default=None, metavar="P_FRAME",
+                    help="fine-grained routing: after the block-level Top-p, Top-p over the "
+                         "frames of each row's kept blocks (abs_route_frames, abs_attend_frames)")
     ap.add_argument("--slack", type=float, default=None,
                     help="per-head slack budget as a fraction of nb^2 (default: the workload's; "
                          "0 turns the fixed fill off)")
@@ -320,6 +323,13 @@ def main():
         wl = dataclasses.replace(wl, slack=args.slack)
     p = float(np.float32(args.p if args.p is not None else wl.p[0]))
     split = args.split is not None
+    frames = args.frames is not None
+    if frames and (split or args.dynamic_slack is not None or wl.dtype != "bf16"):
+        print("--frames runs the plain bf16 path (no --split, no --dynamic-slack)", file=sys.stderr)
+        sys.exit(2)
+    if frames:
+        wl = dataclasses.replace(wl, slack=0.0)
+        args.no_cpu_baseline = True
     if split and args.sched not in (None, "nnz_sorted", "head_phased"):
         print("--split runs on the sorted queues: --sched nnz_sorted or head_phased",
               file=sys.stderr)
@@ -393,9 +403,23 @@ def main():
     side = torch.cuda.Stream(device=dev)
     fork, join = torch.cuda.Event(), torch.cuda.Event()
 
+    fm_t = (torch.empty(int(plan.col_capacity), dtype=torch.int32, device=dev) if frames
+            else None)
+    p_frame = float(np.float32(args.frames)) if frames else None
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
+        if frames:
+            # routing with the frame level, then the prologue and attention in one call
+            A.route_frames(plan, q, k, p, wl.k_floor, p_frame, mask=mask, frame_mask=fm_t, ws=rws)
+            if ev is not None:
+                ev[1].record(stream)
+                ev[2].record(stream)
+            A.attend_frames(plan, q, k, v, mask, fm_t, sched=sched, o=o, ws=aws)
+            if ev is not None:
+                ev[3].record(stream)
+            return
         if pipeline == "beside_route":
             fork.record(stream)            # after the previous step's attention
             side.wait_event(fork)
@@ -451,7 +475,9 @@ def main():
     for i in range(23):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        if dyn is not None:
+        if frames:
+            A.route_frames(plan, q, k, p, wl.k_floor, p_frame, mask=rmask, ws=rws)
+        elif dyn is not None:
             A.route_dynamic(plan, q, k, p, wl.k_floor, args.slack_theta, budget_t, mask=rmask,
                             ws=rws)
         else:
@@ -501,7 +527,7 @@ def main():
         del bws
     bal = {}
     o2 = torch.empty_like(q)
-    sweep = {} if args.timed_only else A.SCHEDULES
+    sweep = {} if (args.timed_only or frames) else A.SCHEDULES
     if split and not args.timed_only:
         sweep = {n: A.SCHEDULES[n] for n in ("nnz_sorted", "head_phased")}
     for name, s in sweep.items():
@@ -542,7 +568,7 @@ def main():
     # dense comparator: the same layer with every block kept (p = 1), our own
     # kernel; context for the explainer's sparse-over-dense attention speedup
     dense = None
-    if not args.timed_only:
+    if not args.timed_only and not frames:
         dmask = A.Mask(plan, dev)
         A.route(plan, q, k, 1.0, 1, 0.0, mask=dmask, ws=rws)
         prepare(dmask, sched)
@@ -580,8 +606,30 @@ def main():
                           f"layer {cb['t_layer_s']:.1f} s"),
                "ms_per_layer": cb["t_layer_s"] * 1e3}
 
+    frame_stats = None
+    if frames:
+        fm = fm_t[:nnz].cpu().numpy()
+        T = wl.grid[0]
+        tblk = wl.block[0]
+        per_plane = plan.nblk[1] * plan.nblk[2]
+        tl = np.array([min(tblk, T - (j // per_plane) * tblk) for j in range(nb)])
+        frame_tok = nvalid / tl                       # real tokens of each frame of a block
+        kept_f = np.array([bin(int(x)).count("1") for x in fm])
+        tok_frames = kept_f * frame_tok[ci]
+        tok_blocks = nvalid[ci]
+        valid_flops = 4.0 * d * float((nvalid[rows_i] * tok_frames).sum())
+        frame_stats = {"p_frame": p_frame, "kept_frames": int(kept_f.sum()),
+                       "frames_of_kept_blocks": int(tl[ci].sum()),
+                       "key_tokens_kept": float(tok_frames.sum()),
+                       "key_tokens_of_kept_blocks": float(tok_blocks.sum()),
+                       "key_fraction_of_block_level": round(float(tok_frames.sum() /
+                                                                  tok_blocks.sum()), 4),
+                       "blocks_without_frames": int((fm == 0).sum()),
+                       "note": "ms_attend_kernel includes the attention prologue (K/V "
+                               "re-layout, key-block lists, schedule)"}
+
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
-    executed = None if split else measured_executed_flop(args.workload, args.sched)
+    executed = None if (split or frames) else measured_executed_flop(args.workload, args.sched)
     route_bytes = 2 * wl.tokens * wl.heads * wl.head_dim * (2 if wl.dtype == "bf16" else 4)
     out = {
         "metric": "ms/attn layer + effective TFLOPS (kept blocks) at Wan2.2 480p shape",
@@ -610,9 +658,12 @@ def main():
         "tflops_valid_pairs_layer": round(valid_flops / (ms_step * 1e-3) / 1e12, 2),
         "roofline": {"bound": "mfma", "achieved": round(eff_attn, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(eff_attn / peak, 4),
-                     "traffic": None if split else measured_traffic(args.workload, args.sched),
+                     "traffic": (None if (split or frames)
+                                 else measured_traffic(args.workload, args.sched)),
                      "kernel": ("attn_bf16_kernel<128,128,true,true> + merge_parts_kernel"
                                 if split else
+                                "attn_bf16_kernel<128,128,true,false,true> (frame masks)"
+                                if frames else
                                 "attn_bf16_kernel<128,128,false,false>"
                                 if args.sched == "head_major"
                                 else "attn_bf16_kernel<128,128,true,false>"),
@@ -630,6 +681,7 @@ def main():
         "mask_parity": parity,
         "imbalance": bal,
         "dynamic_slack": dyn,
+        "frames": frame_stats,
         "ms_per_step_cold": round(float(np.median(cold)), 4) if cold else None,
         "dense_p1": dense,
         "cpu_baseline": cpu,

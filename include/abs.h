@@ -318,6 +318,42 @@ abs_status abs_attend_run_split(const abs_plan* plan, const void* q, const abs_m
 abs_status abs_route_noalloc(const abs_plan* plan, const void* q, const void* k, float p,
                              int32_t k_floor, float slack, const abs_mask* mask, void* stream);
 
+/* Fine-grained Top-p inside the kept blocks (explainer "Core method" part 1,
+ * video-aware block organisation: block-level decisions are combined with
+ * Top-p's fine-grained decisions; the fact-check table repeats "block-level
+ * decisions combined with fine-grained Top-p").  Block routing as abs_route
+ * (no slack fill), then Top-p again over frames: frame tau of key block j is
+ * the part of the block at temporal offset tau (its real tokens with
+ * t % bt == tau).  For every row (b, h, i), the candidates are the frames with
+ * real tokens of the blocks the row keeps; their masses are the softmax, over
+ * the candidates only, of Qp_i . Kf_(j,tau) / sqrt(d) (Kf = mean of k over
+ * the frame's real tokens); ordered by mass (ties: lower j*bt + tau first),
+ * the smallest prefix whose mass reaches p_frame is kept (p_frame == 1 keeps
+ * every candidate), never fewer than k_floor frames, and every frame of block
+ * i.  A kept block may keep no frame.
+ *   p_frame    : in (0, 1]
+ *   frame_mask : device int32 [plan->col_capacity], written: entry e (aligned
+ *                with mask->col_idx) has bit tau set when frame tau of block
+ *                col_idx[e] is kept
+ *   ws         : route workspace of at least plan->route_ws_bytes bytes
+ * Supported: block[0] (frames per block) <= 6 and nb * block[0] <= 1024
+ * (ABS_ENOTSUP otherwise).  Other errors as abs_route. */
+abs_status abs_route_frames(const abs_plan* plan, const void* q, const void* k, float p,
+                            int32_t k_floor, float p_frame, const abs_mask* mask,
+                            int32_t* frame_mask, void* ws, size_t ws_bytes, void* stream);
+
+/* Block-sparse attention restricted to kept frames: as abs_attend, but each
+ * real query token of block i attends to the real keys of the kept frames
+ * (frame_mask from abs_route_frames) of the kept blocks of its row.  Runs the
+ * prologue (K/V re-layout, key-block lists with each row's frames, schedule)
+ * and the attention.  bf16 plans with 128-token blocks, block[0] <= 6
+ * (ABS_ENOTSUP otherwise); any sched; ws of at least plan->attend_ws_bytes
+ * bytes.  Telemetry as abs_attend_run (tiles count kept blocks). */
+abs_status abs_attend_frames(const abs_plan* plan, const void* q, const void* k, const void* v,
+                             const abs_mask* mask, const int32_t* frame_mask, void* o,
+                             int32_t sched, void* ws, size_t ws_bytes, int64_t* telemetry,
+                             void* stream);
+
 /* Static description of a status code. */
 const char* abs_status_string(abs_status status);
 

@@ -124,9 +124,11 @@ def test_route_validation(kw, want):
 
 def test_route_slack_needs_its_scratch():
     plan = _plan()
-    # without the fill the workspace may be smaller than the planned maximum
-    lib = _lib()
-    assert _route(plan, slack=0.15, ws_bytes=plan.route_ws_bytes - 4096) == A.ENOSPACE
+    # the fill needs the probability matrix on top of the means and bitmaps: a
+    # workspace of only that matrix's size is refused (before any launch)
+    _lib()
+    prob_bytes = plan.rows * plan.num_blocks * 4
+    assert _route(plan, slack=0.15, ws_bytes=prob_bytes) == A.ENOSPACE
 
 
 @pytest.mark.parametrize("sched,ws_small,want", [(5, False, A.EINVAL), (-1, False, A.EINVAL),
@@ -308,3 +310,47 @@ def test_route_noalloc_rejects_plans_beyond_its_scratch():
     assert A.status_string(A.ETOOBIG) == "plan too large for the static no-allocation scratch"
     header = open(os.path.join(ROOT, "include", "abs.h")).read()
     assert re.search(r"#define ABS_ROUTE_NOALLOC_SCRATCH_BYTES \(64ull << 20\)", header)
+
+
+def test_route_frames_validation():
+    lib = _lib()
+    plan = _plan()
+    cm = A.CMask(0x100000, 0x200000, 0x300000)
+
+    def call(q=FAKE, p=0.9, kf=4, pf=0.9, fm=FAKE, ws_bytes=None, plan_=plan):
+        nb = plan_.route_ws_bytes if ws_bytes is None else ws_bytes
+        return lib.abs_route_frames(ctypes.byref(plan_), q, FAKE, p, kf, pf, ctypes.byref(cm), fm,
+                                    FAKE, nb, None)
+    assert call(pf=0.0) == A.EINVAL
+    assert call(pf=1.5) == A.EINVAL
+    assert call(pf=math.nan) == A.EINVAL
+    assert call(fm=None) == A.EINVAL
+    assert call(q=None) == A.EINVAL
+    assert call(kf=0) == A.EINVAL
+    assert call(ws_bytes=1024) == A.ENOSPACE
+    # 720p: 660 blocks x 2 frames is more than the 1024 frames a row supports
+    wl = si.WORKLOADS[2]
+    big = A.plan_init(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.block, wl.dtype)
+    assert call(plan_=big) == A.ENOTSUP
+    # more than 8 frames a block
+    st, p9 = _status_of_plan(head_dim=128, grid=(18, 8, 8), block=(16, 2, 4), heads=1,
+                             dtype=A.BF16)
+    assert st == A.OK and call(plan_=p9) == A.ENOTSUP
+
+
+def test_attend_frames_validation():
+    lib = _lib()
+    plan = _plan()
+    cm = A.CMask(0x100000, 0x200000, 0x300000)
+
+    def call(plan_=plan, fm=FAKE, sched=0, ws_bytes=None):
+        nb = plan_.attend_ws_bytes if ws_bytes is None else ws_bytes
+        return lib.abs_attend_frames(ctypes.byref(plan_), FAKE, FAKE, FAKE, ctypes.byref(cm), fm,
+                                     FAKE, sched, FAKE, nb, None, None)
+    assert call(fm=None) == A.EINVAL
+    assert call(sched=9) == A.EINVAL
+    assert call(ws_bytes=1024) == A.ENOSPACE
+    assert call(plan_=_plan(A.F32)) == A.ENOTSUP
+    st, p32 = _status_of_plan(head_dim=128, grid=(8, 8, 8), block=(2, 4, 4), heads=1,
+                              dtype=A.BF16)
+    assert st == A.OK and call(plan_=p32) == A.ENOTSUP    # 32-token blocks
