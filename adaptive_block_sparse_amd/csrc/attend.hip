@@ -88,7 +88,8 @@ template <int D, int BT>
 __global__ __launch_bounds__(256) void kv_relayout_kernel(Geo g, const bf16_t* __restrict__ k,
                                                           const bf16_t* __restrict__ v,
                                                           bf16_t* __restrict__ kc,
-                                                          bf16_t* __restrict__ vc) {
+                                                          bf16_t* __restrict__ vc,
+                                                          float* __restrict__ kn) {
   constexpr int RW = D / 2 + 4;  // row stride in 32-bit words (16-byte aligned, padded)
   __shared__ __attribute__((aligned(16))) uint32_t tile[BT * RW];
   const int blk = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
@@ -121,6 +122,27 @@ __global__ __launch_bounds__(256) void kv_relayout_kernel(Geo g, const bf16_t* _
   __syncthreads();
   const long tile_off = ((long)bh * g.nb + blk) * (long)(D * BT);
   if (which == 0) {
+    // largest norm of the block's keys (padding slots are zero), rounded up by
+    // a relative 2^-12 so that it bounds the norm of the bf16 key exactly
+    {
+      constexpr int TPK = 256 / BT;   // threads per key
+      const int key = threadIdx.x / TPK, part = threadIdx.x % TPK;
+      float ss = 0.f;
+      for (int w = part; w < D / 2; w += TPK) {
+        const uint32_t x = tile[key * RW + w];
+        const float lo = __uint_as_float(x << 16), hi = __uint_as_float(x & 0xffff0000u);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
+      for (int o = 1; o < TPK; o <<= 1) ss += __shfl_xor(ss, o);
+      for (int o = TPK; o < 64; o <<= 1) ss = fmaxf(ss, __shfl_xor(ss, o));
+      __shared__ float wmax[4];
+      if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = ss;
+      __syncthreads();
+      if (threadIdx.x == 0)
+        kn[(long)bh * g.nb + blk] =
+            sqrtf(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))) * (1.0f + 0x1p-12f);
+    }
     uint4* out = reinterpret_cast<uint4*>(kc + tile_off);
     for (int e = threadIdx.x; e < BT * (D / 8); e += 256) {
       const int c = e / BT, key = e % BT;
@@ -559,14 +581,17 @@ __global__ void reset_counter_kernel(int* counter) {
 //     tokens come first in its tile, so chunks and 32-key subtiles of padding
 //     keys, and waves of padding queries, skip their products (and a short
 //     block the copies of its second chunk);
-//   online softmax per query column: running sum in float32, exp2 with
-//     log2(e)/sqrt(d) folded into one FMA, and a lazily moved reference: a
-//     lane's reference moves to the chunk maximum only when that maximum
+//   softmax per query column, running sum in float32.  When the
+//     Cauchy-Schwarz bound on the item's scores (query norms times the head's
+//     largest key norm, K norms from the re-layout) proves that exp2 of every
+//     score lies in [2^-32, 2^32], the probabilities are taken against the
+//     reference 0: one multiply and one exp2 per score, no maxima (FAST walk).
+//     Otherwise (EXACT walk) the reference is a lazily moved running maximum:
+//     a lane's reference moves to the chunk maximum only when that maximum
 //     exceeds it by more than 8 in the exp2 domain, otherwise the chunk's
-//     probabilities are taken against the old reference (at most 2^8, well
-//     inside bf16 and float range) and O^T needs no rescale; O^T and the sum
-//     stay relative to one common reference per query, so the result is the
-//     same softmax;
+//     probabilities are taken against the old reference (at most 2^8) and O^T
+//     needs no rescale.  Either way O^T and the sum stay relative to one
+//     common reference per query, so the result is the same softmax;
 //   O^T (d x queries) += Vt_j P^T, the probabilities converted to bf16 straight
 //     from the accumulator layout (see vt_perm).
 // K/V tiles are double buffered: the direct global->LDS copies of the next
@@ -607,6 +632,7 @@ struct AttnArgs {
   int xcd_local;
   const int* tlist;   // per item: union of the kept key blocks with owners (tile_list_kernel)
   const int* tcount;  // per item: number of entries
+  const float* kn;    // per key block: the largest norm of its keys
   int tlist_cap;      // entries reserved per item
   // split-and-merge mode: queue entries are units {item, t0, t1, slot}
   const int* units;
@@ -642,6 +668,7 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
   constexpr bool BINFO = BT == 128;
   __shared__ int s_binfo[BINFO ? MAX_NB : 1];
   __shared__ int s_item;
+  __shared__ int s_exact;   // some real query of the item needs the running maximum
 
   const Geo& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -675,6 +702,8 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
   };
   if constexpr (BINFO)
     for (int j = tid; j < g.nb; j += C::NT) s_binfo[j] = FRAMES ? block_info_frames(j) : block_info(j);
+  // (the persistent loop clears it again before each item's first barrier)
+  if (tid == 0) s_exact = 0;
   __syncthreads();
 
   const uint32_t sK_base = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)&sK[0][0];
@@ -712,7 +741,10 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
   while (true) {
     int item;
     if (PERSIST) {
-      if (tid == 0) s_item = iter == 0 ? pull() : claimed;
+      if (tid == 0) {
+        s_item = iter == 0 ? pull() : claimed;
+        s_exact = 0;
+      }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       item = __builtin_amdgcn_readfirstlane(s_item);
       if (item >= qlen) break;
@@ -783,11 +815,24 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
     // walk over the item's precomputed union list, read two entries ahead
     const int* tl = a.tlist + (long)item * a.tlist_cap + t0;
     const int nt = SPLIT ? t1 - t0 : ld_scalar(a.tcount, item);
-    int e0 = nt > 0 ? ld_scalar(tl, 0) : -1;
-    int e1 = nt > 1 ? ld_scalar(tl, 1) : -1;
-    int e2 = nt > 2 ? ld_scalar(tl, 2) : -1;
-    if (e0 >= 0) issue(e0, 0);
+    if (nt > 0) issue(ld_scalar(tl, 0), 0);   // the first copy, ahead of the item set-up
 
+
+    // largest key norm of the head (its loads in flight beside the Q loads)
+    float kmx = 0.f;
+    {
+      const float* knh = a.kn + (long)bhh * g.nb;
+      for (int base = 0; base < g.nb; base += 512) {
+        float kv[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int t = base + lane + 64 * x;
+          kv[x] = t < g.nb ? knh[t] : 0.f;
+        }
+#pragma unroll
+        for (int x = 0; x < 8; ++x) kmx = fmaxf(kmx, kv[x]);
+      }
+    }
 
     // this lane's query slot (packed slot order, see packed_slot_offset)
     const int tq = iq / (g.nbh * g.nbw), hq = (iq / g.nbw) % g.nbh, wqb = iq % g.nbw;
@@ -816,196 +861,256 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
       for (int ks = 0; ks < C::KS; ++ks) asm volatile("" ::"v"(qop[ks]));
     }
 
-    f32x16_t o[C::DSUB];
+    // Exponent range.  With c = log2(e)/sqrt(d), every score of query q in the
+    // exp2 domain lies within B = c |q| max_j |k_j| of zero (Cauchy-Schwarz over
+    // the head's keys; the norms are taken from the bf16 values in float32 and
+    // rounded up, and B carries a relative 2^-10 margin for the products'
+    // float32 sums).  When B <= 32 for every real query of the work item, the
+    // probabilities exp2(c s) lie in [2^-32, 2^32], far inside bf16 and float
+    // range, and the softmax needs no running maximum: the item is walked
+    // against the reference 0 (the FAST walk).  Otherwise (or with NaN inputs)
+    // it is walked with the lazily moved running maximum (the EXACT walk).  The
+    // choice is the same for every part of a cut item (it depends on the
+    // queries and the head only).
+    {
+      float q2 = 0.f;
 #pragma unroll
-    for (int u = 0; u < C::DSUB; ++u)
+      for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[u][e] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
-
-    int buf = 0;
-    for (int t = 0; t < nt; ++t) {
-      const int j = e0 & 0xffff;
-      const bool mine = ((e0 >> (17 + half)) & 1) != 0;
-      // fine-grained routing: this wave's row's kept frames of block j
-      const int fmw = FRAMES ? (e0 >> (19 + 6 * half)) & 63 : 0;
-      const int en = e1;
-      if constexpr (SPLIT) tiles += ((e0 >> 17) & 1) + ((e0 >> 18) & 1);   // owned tiles
-      e0 = e1;
-      e1 = e2;
-      e2 = __builtin_amdgcn_readfirstlane(t + 3 < nt ? ld_scalar(tl, t + 3) : -1);
-
-
-      wait_vmcnt<0>();      // this thread's copies of block j have landed
-      wg_barrier();         // ... everyone's; and block j-1's buffer is free
-      if (en >= 0) issue(en, buf ^ 1);
-
-      if (mine && wave_has_q) {
-        const int info = __builtin_amdgcn_readfirstlane(BINFO ? s_binfo[j] : block_info(j));
-        const int nreal = FRAMES ? (info & 255) : info;
-        // fine-grained routing: fpart when this wave's row keeps only some of
-        // the block's frames (the last real key's frame is the last frame); else
-        // the tile runs as without frame masks
-        bool fpart = false;
-        if constexpr (FRAMES) {
-          const int last = (info >> (11 + 6 * ((nreal - 1) >> 5))) & 7;
-          fpart = fmw != (2 << last) - 1;
+        for (int e = 0; e < 8; ++e) {
+          const float x = (float)qop[ks][e];
+          q2 = fmaf(x, x, q2);
         }
-        // kept frames among the real keys of subtiles ta..tb (ta <= tb, both
-        // holding real keys): 2 all, 1 some, 0 none
-        auto frames_in = [&](int ta, int tb) {
-          const int fa = (info >> (8 + 6 * ta)) & 7, fb = (info >> (11 + 6 * tb)) & 7;
-          const int m = ((2 << fb) - 1) & ~((1 << fa) - 1);
-          return (fmw & m) == m ? 2 : ((fmw & m) != 0 ? 1 : 0);
-        };
-        const char* kb = sK[buf] + kread;
-        const char* vb = sV[buf] + vread;
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(q2), __float_as_uint(q2),
+                                                       false, false);
+      q2 = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 #pragma unroll
-        for (int hc = 0; hc < C::NCH; ++hc) {
-          // a chunk whose first slot lies beyond the block's real tokens holds
-          // only padding keys: nothing to add
-          if (hc * C::CHS * 32 >= nreal) continue;
-          // fine-grained routing: a chunk none of whose real keys lies in a kept
-          // frame of this wave's row adds nothing either
-          if (FRAMES && fpart &&
-              frames_in(hc * C::CHS, (hc * C::CHS + 1) * 32 < nreal ? hc * C::CHS + C::CHS - 1
-                                                                     : hc * C::CHS) == 0)
-            continue;
-          // only when the chunk's second subtile holds real keys (of kept
-          // frames) are its score and PV products run (else its scores are the
-          // bias alone and its probabilities zero)
-          bool two = C::CHS == 1 || (hc * C::CHS + 1) * 32 < nreal;
-          if (FRAMES && fpart && two && C::CHS == 2) two = frames_in(hc * 2 + 1, hc * 2 + 1) != 0;
-          // Waves w and w + NW1 share a SIMD and would otherwise run the same
-          // phases in step.  Their priorities alternate: chunk by chunk, one
-          // half leads the score products and the other the softmax and PV
-          // products, so that neither trails the other into the tile barrier.
-          const bool lead_qk = ((hc + half) & 1) != 0;
-          if (lead_qk) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
-          // ---- S^T = K Q^T for the CHS key subtiles of this chunk
-          f32x16_t s[C::CHS];
-          // K operands read from LDS 4 products ahead of use (the order of the
-          // reads and products is pinned)
-          constexpr int NQ = C::CHS * C::KS, PDK = 4 < NQ ? 4 : NQ;
-          auto kaddr = [&](int i) {
-            return reinterpret_cast<const bf16x8_t*>(kb + (i % C::KS) * (2 * BT * 16) +
-                                                     (hc * C::CHS + i / C::KS) * 512);
-          };
-          bf16x8_t kf[PDK];
-#pragma unroll
-          for (int i = 0; i < PDK; ++i) kf[i] = *kaddr(i);
-#pragma unroll
-          for (int t2 = 0; t2 < C::CHS; ++t2) {
-            const int t = hc * C::CHS + t2;
-            // padding keys: add -1e30 through one extra k-step (bias column x ones row).
-            // fmode (fine-grained routing): 1 also masks the keys of frames the
-            // row does not keep, 2 masks every key of the subtile
-            auto add_bias = [&](const f32x16_t& acc, int fmode) {
-              bool ok = 32 * t + l32 < nreal;
-              if (FRAMES && fmode == 2) ok = false;
-              if (FRAMES && fmode == 1) {
-                const int e = block_extent(g, j);
-                const float fs = (float)(((e >> 8) & 255) * ((e >> 16) & 255));
-                // frame of the lane's key slot: floor((s + 1/2) / fs) is exact in
-                // float32 for slots and frame sizes below 256
-                const int f = (int)(((float)(32 * t + l32) + 0.5f) / fs);
-                ok = ok && ((fmw >> f) & 1);
-              }
-              bf16x8_t bias, ones;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) { bias[e] = (__bf16)0.0f; ones[e] = (__bf16)0.0f; }
-              if (hf == 0) ones[0] = (__bf16)1.0f;
-              if (hf == 0 && !ok) bias[0] = (__bf16)(-1.0e30f);
-              return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias, ones, acc, 0, 0, 0);
-            };
-            f32x16_t zero;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) zero[e] = 0.f;
-            if (t2 == 0 || two) {
-              s[t2] = zero;
-#pragma unroll
-              for (int ks = 0; ks < C::KS; ++ks) {
-                const int i = t2 * C::KS + ks;
-                const bf16x8_t av = kf[i % PDK];
-                if (i + PDK < NQ) kf[i % PDK] = *kaddr(i + PDK);
-                s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qop[ks], s[t2], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-              }
-              // only the subtile that holds the block's last real key also
-              // holds padding keys (and, with frame masks, a subtile that
-              // holds keys of a frame its row does not keep)
-              const bool fsub = FRAMES && fpart && frames_in(t, t) != 2;
-              if (32 * (t + 1) > nreal || fsub) s[t2] = add_bias(s[t2], fsub ? 1 : 0);
-            } else {
-              // padding keys only (or, with frame masks, keys of frames the row
-              // does not keep): the scores are the bias alone
-              s[t2] = add_bias(zero, 2);
-            }
-          }
-
-          if (lead_qk) __builtin_amdgcn_s_setprio(0); else __builtin_amdgcn_s_setprio(1);
-          // ---- online softmax over the chunk's keys, per query column
-          // four independent partial maxima (short dependency chains)
-          float mq[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mq[r] = s[0][r];
-#pragma unroll
-          for (int t2 = 0; t2 < C::CHS; ++t2)
-#pragma unroll
-            for (int e = (t2 == 0 ? 4 : 0); e < 16; ++e) mq[e & 3] = vmax(mq[e & 3], s[t2][e]);
-          float mt = vmax(vmax(mq[0], mq[1]), vmax(mq[2], mq[3]));
-          {
-            // the other half of the query column lives in lane l ^ 32
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt),
-                                                             __float_as_uint(mt), false, false);
-            mt = vmax(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-          }
-          // lazily moved reference: only when the chunk maximum exceeds it by
-          // more than 8 in the exp2 domain (probabilities stay <= 2^8)
-          const bool up = !((mt - m_run) * a.c <= 8.0f);   // also true while m_run = -inf
-          const float m_new = up ? mt : m_run;
-          const float alpha = up ? __builtin_amdgcn_exp2f((m_run - m_new) * a.c) : 1.0f;
-          const float mc = m_new * a.c;
-          bf16x8_t pop[2 * C::CHS];
-          float pq[4];   // four independent partial sums
-#pragma unroll
-          for (int t2 = 0; t2 < C::CHS; ++t2)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const float pv = __builtin_amdgcn_exp2f(fmaf(s[t2][e], a.c, -mc));
-              pq[e & 3] = t2 == 0 && e < 4 ? pv : pq[e & 3] + pv;
-              pop[2 * t2 + e / 8][e % 8] = (__bf16)pv;
-            }
-          const float psum = (pq[0] + pq[1]) + (pq[2] + pq[3]);
-          l_run = l_run * alpha + psum;
-          if (up) {
-#pragma unroll
-            for (int u = 0; u < C::DSUB; ++u)
-#pragma unroll
-              for (int e = 0; e < 16; ++e) o[u][e] *= alpha;
-          }
-          m_run = m_new;
-
-          // ---- O^T += Vt P^T over the chunk's keys, subtile by subtile (each
-          // o[u] still sums its 16-key steps in order)
-#pragma unroll
-          for (int t2 = 0; t2 < C::CHS; ++t2) {
-            if (t2 > 0 && !two) break;
-#pragma unroll
-            for (int u = 0; u < C::DSUB; ++u) {
-#pragma unroll
-              for (int st2 = 2 * t2; st2 < 2 * t2 + 2; ++st2) {
-                const int st = hc * 2 * C::CHS + st2;
-                const bf16x8_t av =
-                    *reinterpret_cast<const bf16x8_t*>(vb + st * (2 * D * 16) + u * 512);
-                o[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pop[st2], o[u], 0, 0, 0);
-              }
-            }
-          }
-        }
-      }
-      buf ^= 1;
+      for (int o2 = 1; o2 < 64; o2 <<= 1) kmx = fmaxf(kmx, __shfl_xor(kmx, o2));
+      const float bound = a.c * (sqrtf(q2) * (1.0f + 0x1p-12f)) * kmx * (1.0f + 0x1p-10f);
+      if (__builtin_amdgcn_ballot_w64(qvalid && !(bound <= 32.0f)) != 0 && lane == 0) s_exact = 1;
     }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const bool exact_item = __builtin_amdgcn_readfirstlane(s_exact) != 0;
+    bool any_kept = false;   // the wave's row keeps a block of the walk (wave-uniform)
+
+    f32x16_t o[C::DSUB];
+    float m_run = -INFINITY, l_run = 0.f;   // reference (score units) and sum
+
+    // one walk over the item's union list, read two entries ahead
+    auto walk = [&](auto exact_tag) __attribute__((always_inline)) {
+      constexpr bool EXACT = decltype(exact_tag)::value;
+      int e0 = nt > 0 ? ld_scalar(tl, 0) : -1;
+      int e1 = nt > 1 ? ld_scalar(tl, 1) : -1;
+      int e2 = nt > 2 ? ld_scalar(tl, 2) : -1;
+#pragma unroll
+      for (int u = 0; u < C::DSUB; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[u][e] = 0.f;
+      m_run = EXACT ? -INFINITY : 0.f;
+      l_run = 0.f;
+      int buf = 0;
+      for (int t = 0; t < nt; ++t) {
+        const int j = e0 & 0xffff;
+        const bool mine = ((e0 >> (17 + half)) & 1) != 0;
+        // fine-grained routing: this wave's row's kept frames of block j
+        const int fmw = FRAMES ? (e0 >> (19 + 6 * half)) & 63 : 0;
+        const int en = e1;
+        if constexpr (SPLIT) tiles += ((e0 >> 17) & 1) + ((e0 >> 18) & 1);   // owned tiles
+        any_kept = any_kept || mine;
+        e0 = e1;
+        e1 = e2;
+        e2 = __builtin_amdgcn_readfirstlane(t + 3 < nt ? ld_scalar(tl, t + 3) : -1);
+
+
+        wait_vmcnt<0>();      // this thread's copies of block j have landed
+        wg_barrier();         // ... everyone's; and block j-1's buffer is free
+        if (en >= 0) issue(en, buf ^ 1);
+
+        if (mine && wave_has_q) {
+          const int info = __builtin_amdgcn_readfirstlane(BINFO ? s_binfo[j] : block_info(j));
+          const int nreal = FRAMES ? (info & 255) : info;
+          // fine-grained routing: fpart when this wave's row keeps only some of
+          // the block's frames (the last real key's frame is the last frame); else
+          // the tile runs as without frame masks
+          bool fpart = false;
+          if constexpr (FRAMES) {
+            const int last = (info >> (11 + 6 * ((nreal - 1) >> 5))) & 7;
+            fpart = fmw != (2 << last) - 1;
+          }
+          // kept frames among the real keys of subtiles ta..tb (ta <= tb, both
+          // holding real keys): 2 all, 1 some, 0 none
+          auto frames_in = [&](int ta, int tb) {
+            const int fa = (info >> (8 + 6 * ta)) & 7, fb = (info >> (11 + 6 * tb)) & 7;
+            const int m = ((2 << fb) - 1) & ~((1 << fa) - 1);
+            return (fmw & m) == m ? 2 : ((fmw & m) != 0 ? 1 : 0);
+          };
+          const char* kb = sK[buf] + kread;
+          const char* vb = sV[buf] + vread;
+#pragma unroll
+          for (int hc = 0; hc < C::NCH; ++hc) {
+            // a chunk whose first slot lies beyond the block's real tokens holds
+            // only padding keys: nothing to add
+            if (hc * C::CHS * 32 >= nreal) continue;
+            // fine-grained routing: a chunk none of whose real keys lies in a kept
+            // frame of this wave's row adds nothing either
+            if (FRAMES && fpart &&
+                frames_in(hc * C::CHS, (hc * C::CHS + 1) * 32 < nreal ? hc * C::CHS + C::CHS - 1
+                                                                       : hc * C::CHS) == 0)
+              continue;
+            // only when the chunk's second subtile holds real keys (of kept
+            // frames) are its score and PV products run (else its scores are the
+            // bias alone and its probabilities zero)
+            bool two = C::CHS == 1 || (hc * C::CHS + 1) * 32 < nreal;
+            if (FRAMES && fpart && two && C::CHS == 2) two = frames_in(hc * 2 + 1, hc * 2 + 1) != 0;
+            // Waves w and w + NW1 share a SIMD and would otherwise run the same
+            // phases in step.  Their priorities alternate: chunk by chunk, one
+            // half leads the score products and the other the softmax and PV
+            // products, so that neither trails the other into the tile barrier.
+            const bool lead_qk = ((hc + half) & 1) != 0;
+            if (lead_qk) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
+            // ---- S^T = K Q^T for the CHS key subtiles of this chunk
+            f32x16_t s[C::CHS];
+            // K operands read from LDS 4 products ahead of use (the order of the
+            // reads and products is pinned)
+            constexpr int NQ = C::CHS * C::KS, PDK = 4 < NQ ? 4 : NQ;
+            auto kaddr = [&](int i) {
+              return reinterpret_cast<const bf16x8_t*>(kb + (i % C::KS) * (2 * BT * 16) +
+                                                       (hc * C::CHS + i / C::KS) * 512);
+            };
+            bf16x8_t kf[PDK];
+#pragma unroll
+            for (int i = 0; i < PDK; ++i) kf[i] = *kaddr(i);
+#pragma unroll
+            for (int t2 = 0; t2 < C::CHS; ++t2) {
+              const int t = hc * C::CHS + t2;
+              // padding keys: add -1e30 through one extra k-step (bias column x ones row).
+              // fmode (fine-grained routing): 1 also masks the keys of frames the
+              // row does not keep, 2 masks every key of the subtile
+              auto add_bias = [&](const f32x16_t& acc, int fmode) {
+                bool ok = 32 * t + l32 < nreal;
+                if (FRAMES && fmode == 2) ok = false;
+                if (FRAMES && fmode == 1) {
+                  const int e = block_extent(g, j);
+                  const float fs = (float)(((e >> 8) & 255) * ((e >> 16) & 255));
+                  // frame of the lane's key slot: floor((s + 1/2) / fs) is exact in
+                  // float32 for slots and frame sizes below 256
+                  const int f = (int)(((float)(32 * t + l32) + 0.5f) / fs);
+                  ok = ok && ((fmw >> f) & 1);
+                }
+                bf16x8_t bias, ones;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { bias[e] = (__bf16)0.0f; ones[e] = (__bf16)0.0f; }
+                if (hf == 0) ones[0] = (__bf16)1.0f;
+                if (hf == 0 && !ok) bias[0] = (__bf16)(-1.0e30f);
+                return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias, ones, acc, 0, 0, 0);
+              };
+              f32x16_t zero;
+#pragma unroll
+              for (int e = 0; e < 16; ++e) zero[e] = 0.f;
+              if (t2 == 0 || two) {
+                s[t2] = zero;
+#pragma unroll
+                for (int ks = 0; ks < C::KS; ++ks) {
+                  const int i = t2 * C::KS + ks;
+                  const bf16x8_t av = kf[i % PDK];
+                  if (i + PDK < NQ) kf[i % PDK] = *kaddr(i + PDK);
+                  s[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qop[ks], s[t2], 0, 0, 0);
+                  __builtin_amdgcn_sched_barrier(0);
+                }
+                // only the subtile that holds the block's last real key also
+                // holds padding keys (and, with frame masks, a subtile that
+                // holds keys of a frame its row does not keep)
+                const bool fsub = FRAMES && fpart && frames_in(t, t) != 2;
+                if (32 * (t + 1) > nreal || fsub) s[t2] = add_bias(s[t2], fsub ? 1 : 0);
+              } else {
+                // padding keys only (or, with frame masks, keys of frames the row
+                // does not keep): the scores are the bias alone
+                s[t2] = add_bias(zero, 2);
+              }
+            }
+
+            if (lead_qk) __builtin_amdgcn_s_setprio(0); else __builtin_amdgcn_s_setprio(1);
+            bf16x8_t pop[2 * C::CHS];
+            if constexpr (EXACT) {
+              // ---- online softmax over the chunk's keys, per query column
+              // four independent partial maxima (short dependency chains)
+              float mq[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) mq[r] = s[0][r];
+#pragma unroll
+              for (int t2 = 0; t2 < C::CHS; ++t2)
+#pragma unroll
+                for (int e = (t2 == 0 ? 4 : 0); e < 16; ++e) mq[e & 3] = vmax(mq[e & 3], s[t2][e]);
+              float mt = vmax(vmax(mq[0], mq[1]), vmax(mq[2], mq[3]));
+              {
+                // the other half of the query column lives in lane l ^ 32
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt),
+                                                                 __float_as_uint(mt), false, false);
+                mt = vmax(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+              }
+              // lazily moved reference: only when the chunk maximum exceeds it by
+              // more than 8 in the exp2 domain (probabilities stay <= 2^8)
+              const bool up = !((mt - m_run) * a.c <= 8.0f);   // also true while m_run = -inf
+              const float m_new = up ? mt : m_run;
+              const float alpha = up ? __builtin_amdgcn_exp2f((m_run - m_new) * a.c) : 1.0f;
+              const float mc = m_new * a.c;
+              float pq[4];   // four independent partial sums
+#pragma unroll
+              for (int t2 = 0; t2 < C::CHS; ++t2)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                  const float pv = __builtin_amdgcn_exp2f(fmaf(s[t2][e], a.c, -mc));
+                  pq[e & 3] = t2 == 0 && e < 4 ? pv : pq[e & 3] + pv;
+                  pop[2 * t2 + e / 8][e % 8] = (__bf16)pv;
+                }
+              const float psum = (pq[0] + pq[1]) + (pq[2] + pq[3]);
+              l_run = l_run * alpha + psum;
+              if (up) {
+#pragma unroll
+                for (int u = 0; u < C::DSUB; ++u)
+#pragma unroll
+                  for (int e = 0; e < 16; ++e) o[u][e] *= alpha;
+              }
+              m_run = m_new;
+            } else {
+              // ---- softmax against the reference 0 (see the exponent range above)
+              float pq[4];   // four independent partial sums
+#pragma unroll
+              for (int t2 = 0; t2 < C::CHS; ++t2)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                  const float pv = __builtin_amdgcn_exp2f(s[t2][e] * a.c);
+                  pq[e & 3] = t2 == 0 && e < 4 ? pv : pq[e & 3] + pv;
+                  pop[2 * t2 + e / 8][e % 8] = (__bf16)pv;
+                }
+              l_run += (pq[0] + pq[1]) + (pq[2] + pq[3]);
+            }
+
+            // ---- O^T += Vt P^T over the chunk's keys, subtile by subtile (each
+            // o[u] still sums its 16-key steps in order)
+#pragma unroll
+            for (int t2 = 0; t2 < C::CHS; ++t2) {
+              if (t2 > 0 && !two) break;
+#pragma unroll
+              for (int u = 0; u < C::DSUB; ++u) {
+#pragma unroll
+                for (int st2 = 2 * t2; st2 < 2 * t2 + 2; ++st2) {
+                  const int st = hc * 2 * C::CHS + st2;
+                  const bf16x8_t av =
+                      *reinterpret_cast<const bf16x8_t*>(vb + st * (2 * D * 16) + u * 512);
+                  o[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pop[st2], o[u], 0, 0, 0);
+                }
+              }
+            }
+          }
+        }
+        buf ^= 1;
+      }
+    };
+    if (exact_item) walk(std::true_type{});
+    else walk(std::false_type{});
+    // the reference of O^T and the sum, exp2 domain (-inf: no key)
+    const float m_out = exact_item ? m_run * a.c : (any_kept ? 0.f : -INFINITY);
     if constexpr (!SPLIT) tiles += nA + nB;
     if (PERSIST && tid == 0) claimed = pull();
 
@@ -1025,7 +1130,7 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
           *reinterpret_cast<float4*>(prow + 32 * u + 8 * g4) =
               make_float4(o[u][4 * g4 + 0], o[u][4 * g4 + 1], o[u][4 * g4 + 2], o[u][4 * g4 + 3]);
       if (hf == 0) {
-        ps[2 * BT * D + qi] = m_run * a.c;
+        ps[2 * BT * D + qi] = m_out;
         ps[2 * BT * D + 2 * BT + qi] = l_tot;
       }
     } else if (qvalid) {
@@ -1222,23 +1327,24 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(Geo g, const float* __res
 // ---------------------------------------------------------------------------
 template <int D, int BT>
 static void launch_relayout(const Geo& g, const void* k, const void* v, bf16_t* kc, bf16_t* vc,
-                            hipStream_t s) {
+                            float* kn, hipStream_t s) {
   hipLaunchKernelGGL((kv_relayout_kernel<D, BT>), dim3(g.nb, g.B * g.H, 2), dim3(256), 0, s, g,
-                     (const bf16_t*)k, (const bf16_t*)v, kc, vc);
+                     (const bf16_t*)k, (const bf16_t*)v, kc, vc, kn);
 }
 
 static void launch_relayout_bf16(const Geo& g, const void* k, const void* v, char* ws,
                                  const AttendWs& L, hipStream_t s) {
   bf16_t* kc = (bf16_t*)(ws + L.kc);
   bf16_t* vc = (bf16_t*)(ws + L.vc);
+  float* kn = (float*)(ws + L.kn);
   if (g.d == 128) {
-    if (g.Bt == 128) launch_relayout<128, 128>(g, k, v, kc, vc, s);
-    else if (g.Bt == 64) launch_relayout<128, 64>(g, k, v, kc, vc, s);
-    else launch_relayout<128, 32>(g, k, v, kc, vc, s);
+    if (g.Bt == 128) launch_relayout<128, 128>(g, k, v, kc, vc, kn, s);
+    else if (g.Bt == 64) launch_relayout<128, 64>(g, k, v, kc, vc, kn, s);
+    else launch_relayout<128, 32>(g, k, v, kc, vc, kn, s);
   } else {
-    if (g.Bt == 128) launch_relayout<64, 128>(g, k, v, kc, vc, s);
-    else if (g.Bt == 64) launch_relayout<64, 64>(g, k, v, kc, vc, s);
-    else launch_relayout<64, 32>(g, k, v, kc, vc, s);
+    if (g.Bt == 128) launch_relayout<64, 128>(g, k, v, kc, vc, kn, s);
+    else if (g.Bt == 64) launch_relayout<64, 64>(g, k, v, kc, vc, kn, s);
+    else launch_relayout<64, 32>(g, k, v, kc, vc, kn, s);
   }
 }
 
@@ -1379,6 +1485,8 @@ hipError_t launch_attend_run(const Geo& g, int dtype, const void* q, const void*
     const bool persist = !head_major;
     a.xcd_local = sched == ABS_SCHED_XCD_LOCAL ? 1 : 0;
     a.tlist = (const int*)(ws + L.tlist);
+  a.kn = (const float*)(ws + L.kn);
+    a.kn = (const float*)(ws + L.kn);
     a.tcount = (const int*)(ws + L.tcount);
     a.tlist_cap = tlist_cap(g);
     if (persist) hipLaunchKernelGGL(reset_counter_kernel, dim3(1), dim3(64), 0, s, a.counter);
@@ -1424,6 +1532,7 @@ hipError_t launch_attend_run_split(const Geo& g, const void* q, const abs_mask* 
   a.telem = (long long*)telemetry;
   a.c = (float)(1.4426950408889634 / sqrt((double)g.d));
   a.tlist = (const int*)(ws + L.tlist);
+  a.kn = (const float*)(ws + L.kn);
   a.tcount = (const int*)(ws + L.tcount);
   a.tlist_cap = tlist_cap(g);
   a.units = (const int*)(ws + L.units);

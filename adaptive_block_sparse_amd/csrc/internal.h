@@ -79,6 +79,7 @@ struct AttendWs {
   size_t tlist, tcount;   // bf16: per work item, the union of its rows' kept key
                           // blocks with owners, int32 [groups * 2 nb], and the count [groups]
   size_t icost;           // bf16: per work item, the kept-block count of its rows [groups]
+  size_t kn;              // bf16: per key block, the largest norm of its keys, float [B*H*nb]
   // split-and-merge mode only (sizes 0 otherwise):
   size_t units;           // int4 [groups + max_parts]: {item, t0, t1, slot or -1}
   size_t stab;            // int4 [groups]: per split item {item, first slot, parts, 0}

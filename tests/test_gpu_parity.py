@@ -256,6 +256,53 @@ def test_wide_logit_range_moves_the_reference():
     print("max/mean err", compare_outputs(r["o"], o_ref, geo, rows, wl.heads, wl.dtype))
 
 
+def _exp2_bound(q, k, d):
+    """Per head: log2(e)/sqrt(d) x the largest query norm x the largest key
+    norm (bf16 values, float64): the Cauchy-Schwarz bound on |scores| in the
+    exp2 domain that decides between the kernel's two softmax walks."""
+    qn = np.sqrt((q.astype(np.float64) ** 2).sum(-1)).max(axis=(0, 1))
+    kn = np.sqrt((k.astype(np.float64) ** 2).sum(-1)).max(axis=(0, 1))
+    return 1.4426950408889634 / np.sqrt(d) * qn * kn
+
+
+def test_both_softmax_walks_in_one_launch():
+    """Head 0: random inputs (bound about 20: every item walked against the
+    reference 0).  Head 1: queries and keys along one direction, the keys half
+    aligned and half opposed, scaled so that the bound sits just below 32: the
+    probabilities span about 2^-29 .. 2^29 against the reference 0.  Head 2:
+    the same scaled past 32, walked with the running maximum.  Every output
+    against the oracle, and every schedule gives the same bits."""
+    wl = SMALL["bf16-d128-bt128-ragged"]
+    assert wl.heads == 3
+    d = wl.head_dim
+    rng = np.random.default_rng(31)
+    shape = (1, wl.tokens, wl.heads, d)
+    q = rng.standard_normal(shape).astype(np.float32)
+    k = rng.standard_normal(shape).astype(np.float32)
+    v = rng.standard_normal(shape).astype(np.float32)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    sign = np.where(np.arange(wl.tokens) % 2 == 0, 1.0, -1.0)
+    for h, target in ((1, 29.0), (2, 36.0)):
+        scale = np.sqrt(target * np.sqrt(d) / 1.4426950408889634)   # |q| = |k| = scale
+        q[0, :, h] = scale * u + 0.01 * rng.standard_normal((wl.tokens, d))
+        k[0, :, h] = sign[:, None] * scale * u + 0.01 * rng.standard_normal((wl.tokens, d))
+    qt, kt, vt = (torch.from_numpy(x).to(torch.bfloat16) for x in (q, k, v))
+    bound = _exp2_bound(_np(qt), _np(kt), d)
+    print("exp2-domain bounds per head", bound)
+    assert bound[0] < 30 and 28 < bound[1] < 31.5 and bound[2] > 33
+    p = float(np.float32(wl.p[0]))
+    r = _run(wl, p, wl.k_floor, inputs=(qt, kt, vt))
+    geo = O.geometry(wl.grid, wl.block)
+    rp, ci = r["mask"].to_host()
+    o_ref = O.sparse_attention(_np(r["q"]), _np(r["k"]), _np(r["v"]), geo, rp, ci)
+    rows = range(wl.batch * wl.heads * geo.nb)
+    print("max/mean err", compare_outputs(r["o"], o_ref, geo, rows, wl.heads, wl.dtype))
+    for sched in (A.SCHED_NNZ_SORTED, A.SCHED_HEAD_MAJOR, A.SCHED_XCD_LOCAL):
+        o2 = _run(wl, p, wl.k_floor, sched=sched, inputs=(r["q"], r["k"], r["v"]))["o"]
+        assert np.array_equal(o2, r["o"])
+
+
 def test_nan_input_keeps_mask_well_formed():
     wl = SMALL["bf16-d128-bt128-ragged"]
     q, k, v = si.make_inputs(wl)
