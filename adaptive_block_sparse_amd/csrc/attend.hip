@@ -886,7 +886,10 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
       q2 = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 #pragma unroll
       for (int o2 = 1; o2 < 64; o2 <<= 1) kmx = fmaxf(kmx, __shfl_xor(kmx, o2));
-      const float bound = a.c * (sqrtf(q2) * (1.0f + 0x1p-12f)) * kmx * (1.0f + 0x1p-10f);
+      // (1 + 2^-7): the FAST walk multiplies the bf16 queries by c and rounds
+      // them to bf16 again, which changes each by at most 2^-8 relative
+      const float bound =
+          a.c * (sqrtf(q2) * (1.0f + 0x1p-12f)) * kmx * ((1.0f + 0x1p-10f) * (1.0f + 0x1p-7f));
       if (__builtin_amdgcn_ballot_w64(qvalid && !(bound <= 32.0f)) != 0 && lane == 0) s_exact = 1;
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -1079,7 +1082,7 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
               for (int t2 = 0; t2 < C::CHS; ++t2)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                  const float pv = __builtin_amdgcn_exp2f(s[t2][e] * a.c);
+                  const float pv = __builtin_amdgcn_exp2f(s[t2][e]);
                   pq[e & 3] = t2 == 0 && e < 4 ? pv : pq[e & 3] + pv;
                   pop[2 * t2 + e / 8][e % 8] = (__bf16)pv;
                 }
@@ -1107,8 +1110,17 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
         buf ^= 1;
       }
     };
-    if (exact_item) walk(std::true_type{});
-    else walk(std::false_type{});
+    if (exact_item) {
+      walk(std::true_type{});
+    } else {
+      // FAST walk: c folded into the Q operand, so the products give the
+      // scores in the exp2 domain and each probability is one exp2
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qop[ks][e] = (__bf16)((float)qop[ks][e] * a.c);
+      walk(std::false_type{});
+    }
     // the reference of O^T and the sum, exp2 domain (-inf: no key)
     const float m_out = exact_item ? m_run * a.c : (any_kept ? 0.f : -INFINITY);
     if constexpr (!SPLIT) tiles += nA + nB;
