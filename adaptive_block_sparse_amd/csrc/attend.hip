@@ -585,7 +585,8 @@ __global__ void reset_counter_kernel(int* counter) {
 //     Cauchy-Schwarz bound on the item's scores (query norms times the head's
 //     largest key norm, K norms from the re-layout) proves that exp2 of every
 //     score lies in [2^-32, 2^32], the probabilities are taken against the
-//     reference 0: one multiply and one exp2 per score, no maxima (FAST walk).
+//     reference 0, with log2(e)/sqrt(d) folded into the bf16 Q operand: one
+//     exp2 per score, no maxima (FAST walk).
 //     Otherwise (EXACT walk) the reference is a lazily moved running maximum:
 //     a lane's reference moves to the chunk maximum only when that maximum
 //     exceeds it by more than 8 in the exp2 domain, otherwise the chunk's
