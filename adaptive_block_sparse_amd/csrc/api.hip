@@ -154,10 +154,12 @@ abs_status abs_plan_init(const abs_shape* shape, abs_plan* out) {
   p.rows = rows;
   p.col_capacity = rows * nb;
   // phase width for the head-phased queue: keep the phase's K and V within
-  // about 48 MB, well inside the last-level cache (at 720p, 39 MB a head, one
-  // head a phase ran 0.8 % faster than two and 2.5 % faster than four)
+  // about 24 MB, well inside the last-level cache (at 480p, 20 MB a head, one
+  // head a phase ran 0.6-1.3 % faster than two and 1 % faster than three or
+  // four; at 720p, 39 MB a head, one head ran 0.8 % faster than two and 2.5 %
+  // faster than four)
   const double per_head = 2.0 * (double)tokens * s.head_dim * (s.dtype == ABS_BF16 ? 2 : 4);
-  long long hpp = (long long)(48.0e6 / per_head);
+  long long hpp = (long long)(24.0e6 / per_head);
   if (hpp < 1) hpp = 1;
   if (hpp > (long long)s.batch * s.heads) hpp = (long long)s.batch * s.heads;
   p.heads_per_phase = (int32_t)hpp;

@@ -102,7 +102,8 @@ typedef struct {
   int32_t nblk[3];         /* blocks per axis */
   int32_t num_blocks;      /* nb, blocks per head */
   int32_t block_tokens;    /* Bt = bt*bh*bw */
-  int32_t heads_per_phase; /* phase width used by ABS_SCHED_HEAD_PHASED */
+  int32_t heads_per_phase; /* phase width used by ABS_SCHED_HEAD_PHASED (heads whose
+                              K and V fit in about 24 MB, at least one) */
   int32_t reserved;
   int64_t tokens;          /* N = T*H*W */
   int64_t rows;            /* B*H*nb rows of the block mask */
@@ -234,11 +235,11 @@ abs_status abs_attend(const abs_plan* plan, const void* q, const void* k, const 
                       size_t ws_bytes, int64_t* telemetry, void* stream);
 
 /* The schedule that measured fastest for this plan's shape on MI355X.  With
- * phases that keep about 48 MB of K and V in flight, HEAD_PHASED led on every
- * workload measured (480p by 0.5 % over XCD_LOCAL, the head-imbalance stress
- * by 1-2 %, 720p and the 81-frame 1.3B shape by 5-6 %), so it is returned for
- * every plan; the query stays so that callers need not hard-code it.  Host
- * query. */
+ * phases that keep at most about 24 MB of K and V in flight (one head at the
+ * 480p, 720p and 81-frame shapes), HEAD_PHASED led on every workload measured
+ * (480p by 0.5 % over XCD_LOCAL, the head-imbalance stress by 1-2 %, 720p and
+ * the 81-frame 1.3B shape by 5-6 %), so it is returned for every plan; the
+ * query stays so that callers need not hard-code it.  Host query. */
 abs_status abs_attend_default_sched(const abs_plan* plan, int32_t* sched);
 
 /* Number of workgroups abs_attend_run launches for this plan and schedule on
