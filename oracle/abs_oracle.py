@@ -581,18 +581,25 @@ def dense_attention(Q, K, V) -> np.ndarray:
 # Work schedule
 # --------------------------------------------------------------------------
 def schedule(costs, mode: str, items_per_head: Optional[int] = None,
-             heads_per_phase: int = 1) -> np.ndarray:
+             heads_per_phase: int = 1, n_queues: int = 8) -> np.ndarray:
     """Order in which work items are processed.
 
     Source: FVAttn explainer, part 2 (runtime load balancing: measure each
     head's mask size before the kernel runs and hand the heaviest work out
-    first).  Reading on one GPU: an item is a row of the block mask (or a
-    group of rows of one head processed together), its cost is its kept-block
-    count, and the compute units pull items from one queue.
+    first; heavy heads go to lighter ranks).  Reading on one GPU: an item is a
+    row of the block mask (or a group of rows of one head processed together),
+    its cost is its kept-block count, and the compute units pull items from
+    one queue.
       "head_major": items in their natural order;
       "nnz_sorted": cost descending, ties by item index;
       "head_phased": heads grouped into consecutive phases of heads_per_phase
-         heads; phases in order, inside a phase cost descending, ties by item.
+         heads; phases in order, inside a phase cost descending, ties by item;
+      "xcd_local": one queue per group of compute units (n_queues of them).
+         A head's cost is the sum of its items' costs; heads are placed one by
+         one, cost descending (ties by head index), each onto the queue with
+         the least cost placed so far (ties by queue index).  A queue lists
+         its heads in placement order, each head's items in natural order;
+         the result is queue 0, then queue 1, and so on.
     """
     costs = np.asarray(costs, dtype=np.int64)
     n = costs.shape[0]
@@ -604,6 +611,18 @@ def schedule(costs, mode: str, items_per_head: Optional[int] = None,
         phase = (np.arange(n) // items_per_head) // heads_per_phase
         return np.array(sorted(range(n), key=lambda r: (phase[r], -costs[r], r)),
                         dtype=np.int64)
+    if mode == "xcd_local":
+        heads = n // items_per_head
+        head_cost = [int(costs[h * items_per_head:(h + 1) * items_per_head].sum())
+                     for h in range(heads)]
+        load = [0] * n_queues
+        queues = [[] for _ in range(n_queues)]
+        for h in sorted(range(heads), key=lambda h: (-head_cost[h], h)):
+            x = min(range(n_queues), key=lambda x: (load[x], x))
+            load[x] += head_cost[h]
+            queues[x].append(h)
+        return np.array([h * items_per_head + i for x in range(n_queues) for h in queues[x]
+                         for i in range(items_per_head)], dtype=np.int64)
     raise ValueError(mode)
 
 

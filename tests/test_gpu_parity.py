@@ -213,18 +213,11 @@ def test_pooled_means_and_schedule_array():
         got = aws[: len(groups) * 4].view(torch.int32).cpu().numpy()
         want = O.schedule(costs, mode, items_per_head=gph, heads_per_phase=plan.heads_per_phase)
         np.testing.assert_array_equal(got, want)
-    # XCD-local queues: heads placed longest first onto the least loaded of 8
-    # XCDs; queue x lists its heads' items in placement then natural order
+    # XCD-local queues (one per XCD, eight on MI355X), against the oracle's
     A.attend_prepare(plan, k.to(DEV), v.to(DEV), mask, A.SCHED_XCD_LOCAL, aws)
     torch.cuda.synchronize()
     got = aws[: len(groups) * 4].view(torch.int32).cpu().numpy()
-    hcost = [sum(costs[h * gph:(h + 1) * gph]) for h in range(wl.heads)]
-    load, placed = [0] * 8, [[] for _ in range(8)]
-    for h in sorted(range(wl.heads), key=lambda h: (-hcost[h], h)):
-        x = min(range(8), key=lambda x: (load[x], x))
-        load[x] += hcost[h]
-        placed[x].append(h)
-    want = [h * gph + gl for x in range(8) for h in placed[x] for gl in range(gph)]
+    want = O.schedule(costs, "xcd_local", items_per_head=gph, n_queues=8)
     np.testing.assert_array_equal(got, want)
 
 

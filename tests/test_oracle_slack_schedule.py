@@ -85,3 +85,27 @@ def test_schedule_modes():
     c = [2, 5, 5, 1, 5, 2]
     assert O.schedule(c, "nnz_sorted").tolist() == [1, 2, 4, 0, 5, 3]
     assert O.schedule(c, "head_phased", items_per_head=3).tolist() == [1, 2, 0, 4, 5, 3]
+
+
+def test_schedule_xcd_local_hand_case():
+    """Five heads of two items each on two queues, worked by hand.  Head costs
+    5, 9, 4, 9, 1; placed cost descending with ties by head (1, 3, 0, 2, 4),
+    each onto the least loaded queue with ties by queue: 1 -> q0 (9, 0),
+    3 -> q1 (9, 9), 0 -> q0 (14, 9), 2 -> q1 (14, 13), 4 -> q1 (14, 14).
+    Queue 0 lists heads 1, 0 and queue 1 heads 3, 2, 4, each head's items in
+    natural order."""
+    c = [3, 2, 4, 5, 2, 2, 9, 0, 1, 0]
+    got = O.schedule(c, "xcd_local", items_per_head=2, n_queues=2)
+    assert got.tolist() == [2, 3, 0, 1, 6, 7, 4, 5, 8, 9]
+    # one queue: heads cost descending (ties by head), items natural
+    assert O.schedule(c, "xcd_local", items_per_head=2, n_queues=1).tolist() == \
+        [2, 3, 6, 7, 0, 1, 4, 5, 8, 9]
+    # every item exactly once, for random costs and eight queues
+    rng = np.random.default_rng(3)
+    counts = rng.integers(0, 50, 40 * 7)
+    o = O.schedule(counts, "xcd_local", items_per_head=7)
+    assert sorted(o.tolist()) == list(range(counts.size))
+    # items of one head stay together and in natural order
+    for h in range(40):
+        pos = [int(np.where(o == h * 7 + i)[0][0]) for i in range(7)]
+        assert pos == list(range(pos[0], pos[0] + 7))
