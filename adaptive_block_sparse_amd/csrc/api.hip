@@ -145,9 +145,9 @@ abs_status abs_plan_init(const abs_shape* shape, abs_plan* out) {
   if (nb > MAX_NB) return ABS_ENOTSUP;
   const long long tokens = (long long)s.grid[0] * s.grid[1] * s.grid[2];
   const long long rows = (long long)s.batch * s.heads * nb;
-  // int32 indices: token offsets, CSR positions and element offsets per batch
-  if (rows * nb >= (1ll << 31) || tokens * s.heads * s.head_dim >= (1ll << 31))
-    return ABS_ENOTSUP;
+  // int32 indices: token numbers, CSR positions (rows * nb bounds nnz) and the
+  // per-item key-block lists; element offsets are 64-bit
+  if (rows * nb >= (1ll << 31) || tokens >= (1ll << 31)) return ABS_ENOTSUP;
   p.num_blocks = (int32_t)nb;
   p.block_tokens = (int32_t)bt_tokens;
   p.tokens = tokens;

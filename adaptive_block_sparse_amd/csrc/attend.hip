@@ -667,7 +667,10 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
   // per key block: its number of real tokens (128-token blocks; smaller blocks
   // run two workgroups per CU and keep their LDS)
   constexpr bool BINFO = BT == 128;
-  __shared__ int s_binfo[BINFO ? MAX_NB : 1];
+  // (a real count fits a byte; with frame masks, nb * bt <= MAX_FRAME_KEYS, the
+  // table holds the subtiles' frame ranges as well)
+  using binfo_t = std::conditional_t<FRAMES, int, uint8_t>;
+  __shared__ binfo_t s_binfo[BINFO ? (FRAMES ? MAX_FRAME_KEYS : MAX_NB) : 1];
   __shared__ int s_item;
   __shared__ int s_exact;   // some real query of the item needs the running maximum
 
@@ -702,7 +705,8 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
     return info;
   };
   if constexpr (BINFO)
-    for (int j = tid; j < g.nb; j += C::NT) s_binfo[j] = FRAMES ? block_info_frames(j) : block_info(j);
+    for (int j = tid; j < g.nb; j += C::NT)
+      s_binfo[j] = (binfo_t)(FRAMES ? block_info_frames(j) : block_info(j));
   // (the persistent loop clears it again before each item's first barrier)
   if (tid == 0) s_exact = 0;
   __syncthreads();
@@ -931,7 +935,7 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
         if (en >= 0) issue(en, buf ^ 1);
 
         if (mine && wave_has_q) {
-          const int info = __builtin_amdgcn_readfirstlane(BINFO ? s_binfo[j] : block_info(j));
+          const int info = __builtin_amdgcn_readfirstlane(BINFO ? (int)s_binfo[j] : block_info(j));
           const int nreal = FRAMES ? (info & 255) : info;
           // fine-grained routing: fpart when this wave's row keeps only some of
           // the block's frames (the last real key's frame is the last frame); else

@@ -126,7 +126,7 @@ constexpr int MAX_LPT_HEADS = 1024;
 constexpr int NUNITS = 48;       // counter[NUNITS]: work units of the split-and-merge queue
 constexpr int NSPLIT = 49;       // counter[NSPLIT]: items cut into two or more parts
 constexpr int MAX_SPLIT_PARTS = 1 << 24;   // bound on max_parts (slot indices stay int32)
-constexpr int MAX_NB = 4096;     // key blocks per head supported by the plan
+constexpr int MAX_NB = 8192;     // key blocks per head supported by the plan
 constexpr int MAX_FRAMES = 6;    // fine-grained routing: frames per block (block[0])
 constexpr int MAX_FRAME_KEYS = 1024;   // fine-grained routing: frames per head (nb * bt)
 inline int tlist_cap(const Geo& g) { return 2 * g.nb; }   // union entries per item

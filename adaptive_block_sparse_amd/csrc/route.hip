@@ -1098,7 +1098,8 @@ static void launch_select_d(const Geo& g, dim3 grid, const float* qp, const floa
   ABS_SEL16(8) ABS_SEL16(10) ABS_SEL16(12) ABS_SEL16(16)
 #undef ABS_SEL16
   if (nch <= 32) launch_select_wide<D, 32>(g, grid, qp, kp, bm, cnt, gsum, prob, p, kf, scale, s);
-  else launch_select_wide<D, 64>(g, grid, qp, kp, bm, cnt, gsum, prob, p, kf, scale, s);
+  else if (nch <= 64) launch_select_wide<D, 64>(g, grid, qp, kp, bm, cnt, gsum, prob, p, kf, scale, s);
+  else launch_select_wide<D, 128>(g, grid, qp, kp, bm, cnt, gsum, prob, p, kf, scale, s);
 }
 
 // pooling, then scores + softmax + selection (P kept for a slack fill when
@@ -1110,7 +1111,7 @@ static void launch_route_front(const Geo& g, int dtype, const void* q, const voi
   float* kp = (float*)(ws + L.kp);
   if (dtype == ABS_BF16) launch_pool<bf16_t>(g, q, k, qp, kp, s);
   else launch_pool<float>(g, q, k, qp, kp, s);
-  static_assert(MAX_NB <= 64 * 64, "one wave's registers hold a row of at most 4096 blocks");
+  static_assert(MAX_NB <= 64 * 128, "one wave's registers hold a row of at most 8192 blocks");
   const dim3 grid(route_groups_per_head(g.nb), g.B * g.H);
   const float scale = (float)(1.0 / sqrt((double)g.d));
   uint32_t* bm = (uint32_t*)(ws + L.bitmap);

@@ -124,8 +124,10 @@ typedef struct {
 } abs_mask;
 
 /* Fill *out for the given shape.  Host only, synchronous, no device access.
- * Supported: head_dim in {64, 128}; bt*bh*bw in {32, 64, 128}; nb <= 4096;
- * rows*nb < 2^31. */
+ * Supported: head_dim in {64, 128}; bt*bh*bw in {32, 64, 128}; nb <= 8192;
+ * rows*nb < 2^31 (CSR positions are int32).  Element offsets are 64-bit, so
+ * Q, K, V and O may hold more than 2^31 elements (for example 40 heads of an
+ * 81-frame 1080p latent grid, 81x68x120 tokens: nb = 5535, 3.4e9 elements). */
 abs_status abs_plan_init(const abs_shape* shape, abs_plan* out);
 
 /* Routing (explainer "Core method" part 1, and part 3 when slack > 0).

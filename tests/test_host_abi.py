@@ -90,7 +90,13 @@ def _status_of_plan(**kw):
     (dict(head_dim=96), A.ENOTSUP),
     (dict(block=(2, 4, 6)), A.ENOTSUP),        # 48 tokens per block
     (dict(dtype=7), A.ENOTSUP),
-    (dict(grid=(200, 200, 200), block=(2, 4, 4)), A.ENOTSUP),   # nb > 4096
+    (dict(grid=(200, 200, 200), block=(2, 4, 4)), A.ENOTSUP),   # nb > 8192
+    (dict(grid=(31, 125, 250), block=(2, 8, 8)), A.OK),        # nb = 8192, the largest
+    (dict(grid=(33, 125, 250), block=(2, 8, 8)), A.ENOTSUP),   # nb = 8704
+    # more than 2^31 elements per tensor (64-bit element offsets)
+    (dict(grid=(16, 128, 130), block=(2, 8, 8), heads=64, head_dim=128), A.OK),
+    # rows * nb >= 2^31 (CSR positions are int32)
+    (dict(grid=(31, 125, 250), block=(2, 8, 8), heads=40), A.ENOTSUP),
 ])
 def test_plan_validation(kw, want):
     st, _ = _status_of_plan(**kw)
