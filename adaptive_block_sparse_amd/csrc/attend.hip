@@ -354,7 +354,6 @@ __global__ __launch_bounds__(512) void schedule_kernel(Geo g, const int* __restr
   }
 }
 
-
 // ---------------------------------------------------------------------------
 // Per attention work item (a pair of query blocks of one head, or a single
 // block), the union of its rows' kept key-block lists in ascending order, each
@@ -822,7 +821,6 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
     const int nt = SPLIT ? t1 - t0 : ld_scalar(a.tcount, item);
     if (nt > 0) issue(ld_scalar(tl, 0), 0);   // the first copy, ahead of the item set-up
 
-
     // largest key norm of the head (its loads in flight beside the Q loads)
     float kmx = 0.f;
     {
@@ -928,7 +926,6 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
         e0 = e1;
         e1 = e2;
         e2 = __builtin_amdgcn_readfirstlane(t + 3 < nt ? ld_scalar(tl, t + 3) : -1);
-
 
         wait_vmcnt<0>();      // this thread's copies of block j have landed
         wg_barrier();         // ... everyone's; and block j-1's buffer is free
@@ -1425,7 +1422,6 @@ hipError_t launch_attend_prepare_split(const Geo& g, const void* k, const void* 
   return hipGetLastError();
 }
 
-
 template <int D, int BT>
 static int persistent_grid() {
   int dev = 0;
@@ -1502,7 +1498,6 @@ hipError_t launch_attend_run(const Geo& g, int dtype, const void* q, const void*
     const bool persist = !head_major;
     a.xcd_local = sched == ABS_SCHED_XCD_LOCAL ? 1 : 0;
     a.tlist = (const int*)(ws + L.tlist);
-  a.kn = (const float*)(ws + L.kn);
     a.kn = (const float*)(ws + L.kn);
     a.tcount = (const int*)(ws + L.tcount);
     a.tlist_cap = tlist_cap(g);

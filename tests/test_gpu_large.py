@@ -23,6 +23,8 @@ from parity_utils import compare_masks, compare_outputs, sample_rows
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 DEV = "cuda:0"
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
 
 
 def _np(t):
