@@ -195,3 +195,47 @@ def test_split_full_480p():
     plain = c.o_plain.float().cpu().numpy()
     c.check_rows_equal(o, plain, [r for r in rows if r in whole])
     c.check_rows_equal(o2, plain, [r for r in rows if r in whole2])
+
+
+BLOCKS = [(2, 4, 4), (1, 4, 8), (2, 2, 8), (1, 8, 8), (2, 4, 8), (4, 4, 4),
+          (2, 8, 8), (4, 4, 8), (1, 8, 16), (8, 4, 4)]
+
+
+def _draw(i):
+    """A seeded small bf16 layer with a random cut: block shape, grid (ragged
+    tails, grids below one block along an axis), heads, d, p, k_floor, the
+    longest part and the slot budget (between none and every wanted part)."""
+    rng = np.random.default_rng([2027, i])
+    block = BLOCKS[int(rng.integers(len(BLOCKS)))]
+    while True:
+        grid = tuple(int(rng.integers(1, 3 * b + 1)) for b in block)
+        if grid[0] * grid[1] * grid[2] <= 4000:
+            break
+    heads = int(rng.integers(1, 4))
+    d = int(rng.choice([64, 128]))
+    p = float(np.float32(rng.choice([0.3, 0.6, 0.9, 1.0])))
+    k_floor = int(rng.integers(1, 6))
+    split = int(rng.choice([1, 2, 3, 5, 8]))
+    frac = float(rng.choice([0.0, 0.3, 1.0]))
+    return _wl(400 + i, grid, block, heads, d, (p,), k_floor), split, frac
+
+
+RANDOM = [_draw(i) for i in range(24)]
+
+
+@pytest.mark.parametrize("wl,split,frac", RANDOM,
+                         ids=[f"{w.name}-{w.grid}-{w.block}-h{w.heads}-d{w.head_dim}-p{w.p[0]:.2f}"
+                              f"-S{s}-f{f}" for w, s, f in RANDOM])
+def test_split_random_shapes(wl, split, frac):
+    """Seeded random layers and cuts: the unit table exact (in run_split),
+    every row against the oracle, items left whole bitwise equal to the plain
+    path, both sorted queues bitwise equal."""
+    c = Case(wl)
+    max_parts = int(frac * _wanted(c.counts, split))
+    o, units, cut = c.run_split(split, max_parts)
+    rows = range(c.bh * c.geo.nb)
+    o_ref = O.sparse_attention(*(t.float().numpy() for t in c.inputs), c.geo, c.rp, c.ci)
+    print("max/mean err", compare_outputs(o, o_ref, c.geo, rows, c.wl.heads, "bf16"))
+    c.check_rows_equal(o, c.o_plain.float().cpu().numpy(), c.whole_rows(cut))
+    o2, _, _ = c.run_split(split, max_parts, sched=A.SCHED_HEAD_PHASED)
+    assert np.array_equal(o, o2)
