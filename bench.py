@@ -285,8 +285,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the layer shards by head; see the design notes).", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(a layer would shard by head, each GPU attending its own heads).",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
