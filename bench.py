@@ -158,22 +158,26 @@ def block_valid_counts(grid, block) -> np.ndarray:
     return np.einsum("i,j,k->ijk", *per_axis).ravel()
 
 
-def mfma_probe(dev, iters: int = 40000, workgroups: int = 1024, launches: int = 5):
-    """Sustained bf16 MFMA rate of this GPU on its own (libabs_probe.so, a
-    measurement aid): every SIMD issues v_mfma_f32_32x32x16_bf16 back to back
-    on varied operands.  Median of `launches` timed launches after two untimed
-    ones.  clock64_ghz is the rate of the device's clock64 counter against its
-    wall clock during the product loops."""
+def _probe_lib():
     import ctypes
-    import torch
     path = os.path.join(ROOT, "adaptive_block_sparse_amd", "libabs_probe.so")
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it first (python -m adaptive_block_sparse_amd.build)")
     lib = ctypes.CDLL(path)
-    lib.abs_probe_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
-                                        ctypes.c_void_p, ctypes.c_void_p]
+    V = ctypes.c_void_p
+    lib.abs_probe_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, V, V, V]
+    lib.abs_probe_attn_loop.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, V, V, V]
     lib.abs_probe_wall_clock_khz.argtypes = [ctypes.POINTER(ctypes.c_int32)]
-    out = torch.empty(workgroups * 256, dtype=torch.float32, device=dev)
+    return lib
+
+
+def _time_probe(dev, launch, threads: int, workgroups: int, launches: int):
+    """Median time of `launches` timed launches (after two untimed ones) and
+    the median clock64 rate against the wall clock inside the loops."""
+    import ctypes
+    import torch
+    lib = _probe_lib()
+    out = torch.empty(workgroups * threads, dtype=torch.float32, device=dev)
     clocks = torch.zeros(workgroups * 2, dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream()
     khz = ctypes.c_int32(0)
@@ -183,23 +187,50 @@ def mfma_probe(dev, iters: int = 40000, workgroups: int = 1024, launches: int = 
     for i in range(2 + launches):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        rc = lib.abs_probe_mfma_bf16(iters, workgroups, ctypes.c_void_p(out.data_ptr()),
-                                     ctypes.c_void_p(clocks.data_ptr()),
-                                     ctypes.c_void_p(stream.cuda_stream))
+        rc = launch(lib, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(clocks.data_ptr()),
+                    ctypes.c_void_p(stream.cuda_stream))
         e1.record(stream)
         if rc != 0:
-            raise RuntimeError(f"abs_probe_mfma_bf16 returned {rc}")
+            raise RuntimeError(f"probe launch returned {rc}")
         torch.cuda.synchronize()
         if i >= 2:
             times.append(e0.elapsed_time(e1) * 1e-3)
             c = clocks.cpu().numpy().reshape(-1, 2).astype(np.float64)
             clk.append(float(np.median(c[:, 0] / (c[:, 1] / (khz.value * 1e3)))) / 1e9)
     assert bool(torch.isfinite(out).all())
+    return float(np.median(times)), float(np.median(clk))
+
+
+def mfma_probe(dev, iters: int = 40000, workgroups: int = 512, launches: int = 5):
+    """Sustained bf16 MFMA rate of this GPU on its own (libabs_probe.so, a
+    measurement aid): every wave issues v_mfma_f32_32x32x16_bf16 back to back
+    on varied operands, four independent accumulators.  512 workgroups of four
+    waves are two waves on every SIMD, all resident at once (the attention
+    kernel's occupancy); one wave per SIMD (256) sustains less.  Median of
+    `launches` timed launches after two untimed ones.  clock64_ghz is the rate
+    of the device's clock64 counter against its wall clock during the loops."""
+    t, clk = _time_probe(dev, lambda lib, o, c, s: lib.abs_probe_mfma_bf16(iters, workgroups, o, c, s),
+                         256, workgroups, launches)
     flop = workgroups * 4 * iters * 4 * 32 * 32 * 16 * 2
-    t = float(np.median(times))
-    return {"tflops": round(flop / t / 1e12, 1), "clock64_ghz": round(float(np.median(clk)), 3),
+    return {"tflops": round(flop / t / 1e12, 1), "clock64_ghz": round(clk, 3),
             "ms_per_launch": round(t * 1e3, 3), "iters": iters, "workgroups": workgroups,
-            "launches": launches}
+            "waves_per_simd": workgroups // 256, "launches": launches}
+
+
+def attn_loop_probe(dev, queries_per_wave: int = 32, iters: int = 12000, workgroups: int = 256,
+                    launches: int = 5):
+    """Rate of the attention kernel's per-subtile arithmetic on its own
+    (libabs_probe.so): scores, FAST-walk softmax and PV products of one 32-key
+    subtile a round, operands from LDS, with no copies, barrier, padding or
+    work items.  32 queries per wave: two waves per SIMD, as in the kernel; 64:
+    one wave per SIMD holding two query groups."""
+    threads = 512 if queries_per_wave == 32 else 256
+    t, clk = _time_probe(dev, lambda lib, o, c, s: lib.abs_probe_attn_loop(
+        queries_per_wave, iters, workgroups, o, c, s), threads, workgroups, launches)
+    flop = workgroups * iters * (threads // 64) * (queries_per_wave // 32) * 16 * 32768
+    return {"tflops": round(flop / t / 1e12, 1), "clock64_ghz": round(clk, 3),
+            "ms_per_launch": round(t * 1e3, 3), "queries_per_wave": queries_per_wave,
+            "iters": iters, "workgroups": workgroups, "launches": launches}
 
 
 def cpu_baseline(wl, p, inputs, rp, ci, budget_s=20.0):
@@ -278,10 +309,12 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for HBM counter scaling)")
     ap.add_argument("--mfma-peak", action="store_true",
-                    help="run only the MFMA probe: the bf16 rate this GPU sustains on its own "
-                         "and its shader clock meanwhile")
+                    help="run only the probes: the bf16 MFMA rate this GPU sustains on its own "
+                         "at one, two and three waves per SIMD and its clock meanwhile, and the "
+                         "attention kernel's per-subtile arithmetic alone at 32 and 64 queries "
+                         "per wave")
     ap.add_argument("--probe-launches", type=int, default=5,
-                    help="timed launches of the MFMA probe (about 14 ms each)")
+                    help="timed launches of each probe (about 10 ms each)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -305,7 +338,11 @@ def main():
         print(json.dumps({"copy_bytes": 1 << 30, "launches": 3}))
         return
     if args.mfma_peak:
-        print(json.dumps({"mfma_probe_bf16": mfma_probe(dev, launches=args.probe_launches)}))
+        n = args.probe_launches
+        print(json.dumps({"mfma_probe_bf16": [mfma_probe(dev, workgroups=w, launches=n)
+                                              for w in (256, 512, 768)],
+                          "attn_loop_probe": [attn_loop_probe(dev, qpw, launches=n)
+                                              for qpw in (32, 64)]}))
         return
 
     import adaptive_block_sparse_amd as A
@@ -591,6 +628,9 @@ def main():
     # the bf16 MFMA rate this GPU sustains on its own (power-limited clock),
     # reported beside the data-sheet peak
     probe = mfma_probe(dev) if (not args.timed_only and wl.dtype == "bf16") else None
+    # ... and what the attention kernel's inner arithmetic reaches with nothing
+    # around it (no copies, barrier, padding or work items)
+    loop = attn_loop_probe(dev) if (not args.timed_only and wl.dtype == "bf16") else None
 
     cpu = None
     parity = None
@@ -672,8 +712,10 @@ def main():
                      "frac_valid_pairs": round(valid_flops / (t_attn * 1e-3) / 1e12 / peak, 4),
                      "frac_executed": (round(executed / (t_attn * 1e-3) / 1e12 / peak, 4)
                                        if executed else None),
-                     "probe_peak": probe["tflops"] if probe else None},
+                     "probe_peak": probe["tflops"] if probe else None,
+                     "loop_probe": loop["tflops"] if loop else None},
         "mfma_probe_bf16": probe,
+        "attn_loop_probe": loop,
         "route_hbm": {"bytes_read_qk": route_bytes,
                       "gbs_algorithmic_alone": round(route_bytes / (t_route_alone * 1e-3) / 1e9, 1),
                       "frac_of_8tbs_alone": round(route_bytes / (t_route_alone * 1e-3) / 1e9

@@ -46,5 +46,11 @@ def test_bench_line_contract():
 
 def test_bench_mfma_probe():
     d = _bench("--mfma-peak", "--probe-launches", "2")
-    p = d["mfma_probe_bf16"]
-    assert 100.0 < p["tflops"] < 2600.0
+    runs = d["mfma_probe_bf16"]
+    assert [p["waves_per_simd"] for p in runs] == [1, 2, 3]
+    for p in runs:
+        assert 100.0 < p["tflops"] < 2600.0
+    loops = d["attn_loop_probe"]
+    assert [p["queries_per_wave"] for p in loops] == [32, 64]
+    for p in loops:
+        assert 100.0 < p["tflops"] < 2600.0

@@ -450,3 +450,8 @@ def test_mfma_probe_runs():
     print("probe", r)
     assert r["tflops"] > 0
     assert 0.5 < r["clock64_ghz"] < 3.0
+    for qpw in (32, 64):
+        r = bench.attn_loop_probe(DEV, qpw, iters=100, workgroups=256, launches=2)
+        print("loop probe", r)
+        assert r["tflops"] > 0
+        assert 0.5 < r["clock64_ghz"] < 3.0

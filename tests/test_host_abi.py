@@ -39,7 +39,7 @@ def test_probe_library_exports_its_header():
     lib = ctypes.CDLL(path)
     header = open(os.path.join(ROOT, "include", "abs_probe.h")).read()
     declared = set(re.findall(r"^\s*int\s+(abs_probe_\w+)\s*\(", header, re.M))
-    assert declared == {"abs_probe_mfma_bf16", "abs_probe_wall_clock_khz"}
+    assert declared == {"abs_probe_mfma_bf16", "abs_probe_attn_loop", "abs_probe_wall_clock_khz"}
     for name in declared:
         assert hasattr(lib, name)
     f = lib.abs_probe_mfma_bf16
@@ -48,6 +48,11 @@ def test_probe_library_exports_its_header():
     # invalid arguments are rejected before any launch
     assert f(0, 4, FAKE, FAKE, None) == 1
     assert f(10, 0, FAKE, FAKE, None) == 1
+    g = lib.abs_probe_attn_loop
+    g.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    for qpw, iters, wgs in ((16, 10, 4), (48, 10, 4), (32, 0, 4), (64, 10, 0)):
+        assert g(qpw, iters, wgs, FAKE, FAKE, None) == 1
     assert f(10, 4, None, FAKE, None) == 1
     assert lib.abs_probe_wall_clock_khz(None) == 1
 
