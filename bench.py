@@ -295,10 +295,12 @@ def main():
     ap.add_argument("--slack-cap", type=int, default=None,
                     help="cap on pairs the dynamic fill adds (default: 5%% of the base mask)")
     ap.add_argument("--pipeline", default="beside_route",
-                    choices=["beside_route", "after_route", "serial"],
+                    choices=["beside_route", "beside_route_only", "after_route", "serial"],
                     help="where the mask-independent K/V re-layout runs: on a second stream "
-                         "beside routing (default); on a second stream after routing, beside "
-                         "the mask-dependent schedule; or after routing on one stream")
+                         "beside routing and the mask-dependent schedule kernels (default); "
+                         "beside routing only (the schedule kernels wait for it); on a second "
+                         "stream after routing, beside the schedule kernels; or after routing "
+                         "on one stream")
     ap.add_argument("--no-overlap", action="store_true",
                     help="the same as --pipeline serial")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -432,11 +434,13 @@ def main():
                    tel0.cpu().numpy().reshape(-1, 4))["busy_max_over_mean"], 4)}
 
     # The K/V re-layout does not depend on the mask, so it can run on a second
-    # stream (default priority).  Beside routing (the default), routing and the
-    # re-layout share HBM bandwidth: the routing kernels take longer, but the
-    # two finish sooner than one after the other (480p, same box: 0.45 against
-    # 0.47 ms from the step's start to the attention launch, either the
-    # re-layout beside the schedule kernels or everything on one stream).
+    # stream (default priority).  Beside routing and the schedule kernels (the
+    # default), routing and the re-layout share HBM bandwidth: the routing
+    # kernels take longer, but the two finish sooner than one after the other
+    # (480p, same box: 0.42-0.43 ms from the step's start to the attention
+    # launch, against 0.44-0.46 with the schedule kernels waiting for the
+    # re-layout and 0.47 with the re-layout beside the schedule kernels only or
+    # everything on one stream).
     pipeline = "serial" if (split or args.no_overlap) else args.pipeline
     side = torch.cuda.Stream(device=dev)
     fork, join = torch.cuda.Event(), torch.cuda.Event()
@@ -458,7 +462,7 @@ def main():
             if ev is not None:
                 ev[3].record(stream)
             return
-        if pipeline == "beside_route":
+        if pipeline in ("beside_route", "beside_route_only"):
             fork.record(stream)            # after the previous step's attention
             side.wait_event(fork)
             A.attend_relayout(plan, k, v, aws, stream=side)
@@ -478,6 +482,11 @@ def main():
             A.attend_schedule(plan, mask, sched, aws)
             stream.wait_event(join)
         elif pipeline == "beside_route":
+            # the schedule kernels need only the mask: they run beside the
+            # re-layout's tail, and attention waits for both
+            A.attend_schedule(plan, mask, sched, aws)
+            stream.wait_event(join)
+        elif pipeline == "beside_route_only":
             stream.wait_event(join)
             A.attend_schedule(plan, mask, sched, aws)
         else:

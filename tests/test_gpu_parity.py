@@ -368,7 +368,8 @@ def test_full_workload_parity(cfg, p):
             o2 = _run(wl, p, wl.k_floor, sched=s, inputs=inputs)["o"]
             assert np.array_equal(o2, r["o"])
         # and the benchmark's pipeline: the K/V re-layout on a second stream
-        # beside routing, joined by an event before the schedule
+        # beside routing and the schedule kernels, joined by an event before
+        # the attention run
         qd, kd, vd = (t.to(DEV) for t in inputs)
         plan = r["plan"]
         sched = A.default_sched(plan)
@@ -381,8 +382,8 @@ def test_full_workload_parity(cfg, p):
         A.attend_relayout(plan, kd, vd, ws, stream=side)
         join.record(side)
         m3 = A.route(plan, qd, kd, p, wl.k_floor)
-        main.wait_event(join)
         A.attend_schedule(plan, m3, sched, ws)
+        main.wait_event(join)
         A.attend_run(plan, qd, kd, m3, o3, sched, ws)
         torch.cuda.synchronize()
         assert np.array_equal(o3.float().cpu().numpy(), r["o"])
