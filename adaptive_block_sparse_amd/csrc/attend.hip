@@ -645,14 +645,24 @@ __device__ __forceinline__ int ld_scalar(const int* p, long i) {
   return ((cint_t*)(const void*)p)[i];
 }
 
-// Copy 16 bytes per lane from global memory into LDS at lds_base + 16*lane.
-// Written as inline asm so that the compiler does not treat the transfer as
-// an LDS store it must wait for before every LDS read; completion is tracked
-// explicitly with s_waitcnt vmcnt.  The instruction writes no registers.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+// Copy 16 bytes per lane from global memory at base + voff into LDS at
+// lds_base + 16*lane; base and lds_base are the same in every lane.  Written as
+// inline asm so that the compiler does not treat the transfer as an LDS store
+// it must wait for before every LDS read; completion is tracked explicitly
+// with s_waitcnt vmcnt.  The instruction writes no registers.  The address is
+// a scalar base plus a 32-bit offset per lane: issuing a copy holds up the
+// issuing wave, and this form, with half the per-lane address data of a full
+// 64-bit address, issues faster.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
+  const uint64_t b = (uint64_t)base;
+  // (readfirstlane returns int: each half goes through uint32_t so that the
+  // low half is zero-extended, not sign-extended, into the 64-bit base)
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory", "m0");
 }
 
@@ -804,14 +814,14 @@ __global__ __launch_bounds__(128 * (BT / 32), 2) void attn_bf16_kernel(AttnArgs 
 #pragma unroll
         for (int rr = 0; rr < C::ROUNDS; ++rr) {
           const int off = (rr * C::NW + w) * 1024;
-          dma16(ks + off + lane * 16, sK_base + buf * C::TILE + off);
+          dma16(ks, off + lane * 16, sK_base + buf * C::TILE + off);
         }
       }
 #pragma unroll
       for (int rr = 0; rr < C::ROUNDS; ++rr) {
         if (rr < V2 || !short_blk) {
           const int off = (rr * C::NW + w) * 1024;
-          dma16(vs + off + lane * 16, sV_base + buf * C::TILE + off);
+          dma16(vs, off + lane * 16, sV_base + buf * C::TILE + off);
         }
       }
     };
