@@ -163,7 +163,7 @@ __global__ __launch_bounds__(NG == 1 ? 512 : 256)
 
 extern "C" int abs_probe_attn_loop(int32_t queries_per_wave, int32_t iters, int32_t workgroups,
                                    float* out, int64_t* clocks, void* stream) {
-  if (iters <= 0 || workgroups <= 0 || !out || !clocks ||
+  if (iters <= 0 || workgroups <= 0 || workgroups > ABS_PROBE_MAX_WORKGROUPS || !out || !clocks ||
       (queries_per_wave != 32 && queries_per_wave != 64))
     return 1;
   if (queries_per_wave == 32)
@@ -177,7 +177,8 @@ extern "C" int abs_probe_attn_loop(int32_t queries_per_wave, int32_t iters, int3
 
 extern "C" int abs_probe_mfma_bf16(int32_t iters, int32_t workgroups, float* out,
                                    int64_t* clocks, void* stream) {
-  if (iters <= 0 || workgroups <= 0 || !out || !clocks) return 1;
+  if (iters <= 0 || workgroups <= 0 || workgroups > ABS_PROBE_MAX_WORKGROUPS || !out || !clocks)
+    return 1;
   hipLaunchKernelGGL(mfma_peak_kernel, dim3(workgroups), dim3(256), 0, (hipStream_t)stream,
                      iters, out, clocks);
   return hipGetLastError() == hipSuccess ? 0 : 4;

@@ -19,6 +19,10 @@
 extern "C" {
 #endif
 
+/* Largest workgroup count either probe accepts (keeps every thread's output
+ * index below 2^31). */
+#define ABS_PROBE_MAX_WORKGROUPS (1 << 21)
+
 /* Launches `workgroups` workgroups of 256 threads (4 waves); each wave runs
  * `iters` rounds of 4 products of 32x32x16, i.e. 4 * 32768 * iters flop.
  *   out    : device, float32 [workgroups * 256], one sum of the accumulators
@@ -27,8 +31,9 @@ extern "C" {
  *            counts and the wall-clock ticks (wall_clock64, whose rate is
  *            hipDeviceAttributeWallClockRate) of its product loop.
  * Caller-owned buffers; asynchronous on `stream` (a hipStream_t, NULL for the
- * default stream).  Returns 0, 1 for invalid arguments (no launch) or 4 for
- * a launch error. */
+ * default stream).  Returns 0, 1 for invalid arguments (workgroups outside
+ * [1, ABS_PROBE_MAX_WORKGROUPS] among them; no launch) or 4 for a launch
+ * error. */
 int abs_probe_mfma_bf16(int32_t iters, int32_t workgroups, float* out, int64_t* clocks,
                         void* stream);
 
@@ -48,8 +53,9 @@ int abs_probe_mfma_bf16(int32_t iters, int32_t workgroups, float* out, int64_t* 
  * occupancy), so `workgroups` a multiple of the CU count runs whole rounds.
  *   out    : device, float32 [workgroups * (8 or 4) * 64];
  *   clocks : device, int64 [workgroups * 2], as for abs_probe_mfma_bf16.
- * Returns 0, 1 for invalid arguments (queries_per_wave not 32 or 64, no
- * launch) or 4 for a launch error. */
+ * Returns 0, 1 for invalid arguments (queries_per_wave not 32 or 64,
+ * workgroups outside [1, ABS_PROBE_MAX_WORKGROUPS]; no launch) or 4 for a
+ * launch error. */
 int abs_probe_attn_loop(int32_t queries_per_wave, int32_t iters, int32_t workgroups, float* out,
                         int64_t* clocks, void* stream);
 

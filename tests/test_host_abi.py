@@ -48,10 +48,12 @@ def test_probe_library_exports_its_header():
     # invalid arguments are rejected before any launch
     assert f(0, 4, FAKE, FAKE, None) == 1
     assert f(10, 0, FAKE, FAKE, None) == 1
+    assert f(10, (1 << 21) + 1, FAKE, FAKE, None) == 1
     g = lib.abs_probe_attn_loop
     g.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                   ctypes.c_void_p, ctypes.c_void_p]
-    for qpw, iters, wgs in ((16, 10, 4), (48, 10, 4), (32, 0, 4), (64, 10, 0)):
+    for qpw, iters, wgs in ((16, 10, 4), (48, 10, 4), (32, 0, 4), (64, 10, 0),
+                            (32, 10, (1 << 21) + 1)):
         assert g(qpw, iters, wgs, FAKE, FAKE, None) == 1
     assert f(10, 4, None, FAKE, None) == 1
     assert lib.abs_probe_wall_clock_khz(None) == 1
