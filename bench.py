@@ -722,7 +722,15 @@ def main():
                      "frac_executed": (round(executed / (t_attn * 1e-3) / 1e12 / peak, 4)
                                        if executed else None),
                      "probe_peak": probe["tflops"] if probe else None,
-                     "loop_probe": loop["tflops"] if loop else None},
+                     "loop_probe": loop["tflops"] if loop else None,
+                     # executed MFMA rate against what this machine sustains in the
+                     # same run (box-independent, unlike the data-sheet fraction)
+                     "frac_executed_of_probe": (
+                         round(executed / (t_attn * 1e-3) / 1e12 / probe["tflops"], 4)
+                         if (executed and probe) else None),
+                     "frac_executed_of_loop_probe": (
+                         round(executed / (t_attn * 1e-3) / 1e12 / loop["tflops"], 4)
+                         if (executed and loop) else None)},
         "mfma_probe_bf16": probe,
         "attn_loop_probe": loop,
         "route_hbm": {"bytes_read_qk": route_bytes,
