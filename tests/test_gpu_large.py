@@ -6,7 +6,10 @@
   attention kernel's block table.
 * A layer whose Q, K, V and O tensors hold more than 2^31 elements each (64
   heads x 266 240 tokens x d = 128): every element offset of the pooling, the
-  K/V re-layout and the attention loads and stores must be 64-bit.  Heads 0
+  K/V re-layout and the attention loads and stores must be 64-bit, and the
+  attention kernel's tile copies, addressed as a 64-bit scalar base plus a
+  32-bit lane offset, reach tiles whose address has bit 31 of its low half
+  set (the base's low half must be zero-extended, not sign-extended).  Heads 0
   and 63 carry the seeded synthetic inputs and are checked against the oracle
   (pooled means, the whole mask outside the exemption rule, sampled outputs
   that include the highest token offsets); the other heads are seeded random
